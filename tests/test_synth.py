@@ -47,7 +47,7 @@ def test_bf16_round_to_nearest_even():
     np.testing.assert_array_equal(got, np.array([1.0, 1.0, 1.0 + 2**-6, 1.0 + 2**-7, -2.5, 0.0], dtype=np.float32))
     y = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
     r = bf16_bits_to_f32(f32_to_bf16_bits(y))
-    assert np.max(np.abs(r - y) / np.abs(y)) <= 2**-9
+    assert np.max(np.abs(r - y) / np.abs(y)) <= 2**-8   # unit roundoff of an 8-bit significand
 
 
 def test_softmax_topk_routing():
