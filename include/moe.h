@@ -1,0 +1,166 @@
+/*
+ * moe.h — C ABI of the routed mixture-of-experts expert computation on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (kernelindex.com operation pages):
+ *   "Sparse expert dispatch and combine" (description): tokens routed to an
+ *     expert are extracted, pass through a gate_up projection, a gated GLU
+ *     with clamping and a down projection, and are accumulated back into the
+ *     output rows of their tokens.
+ *   "MoE training token repeat and expert computation" (description): every
+ *     token is repeated once per chosen expert, each expert selects its rows,
+ *     runs a SwiGLU FFN, and the routing weights scale the expert outputs
+ *     before the sum over the chosen experts.
+ *   "MoE expert parallel execution backward" (description): gradients with
+ *     respect to hidden_states, topk_weights and the gate, up and down weights.
+ *
+ * Notation: T tokens, H hidden size, I intermediate size, E experts, K experts
+ * per token (the workload lines' hidden_size, intermediate_size,
+ * num_local_experts / num_experts / n_routed_experts, num_experts_per_tok).
+ * S = T*K slots; slot s = t*K + k is the k-th copy of token t.
+ *
+ *   out[t] = sum_k w[t,k] * Wd[e] . phi(Wgu[e] . x_t),   e = ids[t,k]
+ *
+ * phi splits the 2I gate_up outputs into gate g and up u (layout flag) and is
+ *   MOE_SWIGLU:      g * sigmoid(g) * u
+ *   MOE_CLAMPED_GLU: gc = min(g, L), uc = clamp(u, -L, L),
+ *                    (uc + 1) * gc * sigmoid(alpha * gc)     (L = clamp_limit)
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major, contiguous, 16-byte
+ *     aligned.  hidden/out/d_out/d_hidden [T,H]; w_gate_up/d_w_gate_up
+ *     [E,2I,H]; w_down/d_w_down [E,H,I]; topk_ids int32 [T,K];
+ *     topk_weights/d_topk_weights fp32 [T,K].  Activations, weights and
+ *     d_hidden have the descriptor's dtype (bf16 or fp32); the weight
+ *     gradients have its grad_dtype.
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory, never frees, and keeps no pointer after a call returns.
+ *   - Outputs are fully overwritten (never accumulated).
+ *   - Calls are asynchronous on `stream` and never synchronise the host,
+ *     except moe_check_device_status.  Calls are re-entrant given distinct
+ *     workspaces; two calls sharing one workspace must be stream-ordered.
+ *   - Host-checkable errors are reported before any launch, with nothing
+ *     written: MOE_ERR_INVALID_ARG (null pointer where one is required,
+ *     T<0, K<1, E<1, H<1, I<1, bad enum, misaligned pointer),
+ *     MOE_ERR_UNSUPPORTED (H or I not a multiple of 8, E > 1024, K > 64,
+ *     S >= 2^31), MOE_ERR_WORKSPACE (ws_bytes below the required size).
+ *     A failed kernel launch returns MOE_ERR_HIP.
+ *   - An expert id outside [0,E) is found on the device: its slot is dropped
+ *     from every sum, a flag is set in the workspace, and
+ *     moe_check_device_status reports MOE_ERR_BAD_EXPERT_ID; the outputs of
+ *     that call are then unspecified.
+ *   - T = 0 is valid: nothing is launched for the activations; moe_bwd still
+ *     writes zero weight gradients.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4,
+  MOE_ERR_BAD_EXPERT_ID = 5
+} moe_status_t;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype_t;
+typedef enum { MOE_SWIGLU = 0, MOE_CLAMPED_GLU = 1 } moe_act_t;
+/* CONCAT: rows [0,I) of w_gate_up[e] are the gate, rows [I,2I) the up
+ * projection.  INTERLEAVED: row 2j is gate column j, row 2j+1 up column j. */
+typedef enum { MOE_GU_CONCAT = 0, MOE_GU_INTERLEAVED = 1 } moe_gu_layout_t;
+
+typedef struct {
+  int64_t T, H, I, E, K;
+  int32_t dtype;      /* moe_dtype_t */
+  int32_t act;        /* moe_act_t */
+  int32_t gu_layout;  /* moe_gu_layout_t */
+  float clamp_limit;  /* L of the clamped GLU (7.0 for the gpt-oss shapes) */
+  float glu_alpha;    /* alpha of the clamped GLU (1.702) */
+  int32_t grad_dtype; /* moe_dtype_t of d_w_gate_up / d_w_down (accumulation is
+                         always fp32; MOE_F32 stores the fp32 sums) */
+} moe_desc_t;
+
+/* Sizes in bytes of the workspaces moe_fwd and moe_bwd need, and of the
+ * optional `saved` buffer (the gate_up projection outputs Z, fp32 [S,2I] in
+ * expert-sorted slot order) that moe_fwd can fill for moe_bwd.  Any output pointer may be NULL.
+ * The routing part of both workspaces is moe_route_workspace_size(). */
+moe_status_t moe_workspace_size(const moe_desc_t* desc, size_t* fwd_ws,
+                                size_t* bwd_ws, size_t* saved_bytes);
+moe_status_t moe_route_workspace_size(const moe_desc_t* desc, size_t* route_ws);
+
+/* Expert histogram and stable grouping of the slots by expert — the "masked
+ * indexing" / "sparse token extraction" step of the pages' descriptions.
+ * Outputs (device, int32):
+ *   counts[E]       slots routed to each expert
+ *   offsets[E+1]    exclusive prefix sum of counts
+ *   sorted_slot[S]  slots in expert order; ascending slot id inside an expert
+ *   inv_pos[S]      position of slot s in sorted_slot (-1 for a bad id)
+ * Bit-exact and deterministic.  Any of the four outputs may be NULL (then not
+ * written).  ws: at least moe_route_workspace_size() bytes. */
+moe_status_t moe_route(const moe_desc_t* desc, const int32_t* topk_ids,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                       int32_t* inv_pos, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Forward: out [T,H] = sum_k w[t,k] * FFN_{ids[t,k]}(hidden[t]).
+ * Routing, gate_up projection with the gated activation, down projection with
+ * the routing weight, and a deterministic per-token sum over the K slots
+ * (fp32, k order, one rounding).  `saved` may be NULL; if given (saved_bytes
+ * from moe_workspace_size) it receives Z for moe_bwd. */
+moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden,
+                     const int32_t* topk_ids, const float* topk_weights,
+                     const void* w_gate_up, const void* w_down, void* out,
+                     void* saved, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Backward of moe_fwd given d_out = dL/dout [T,H]:
+ *   d_hidden [T,H], d_topk_weights fp32 [T,K] (<d_out[t], expert output of
+ *   slot s>), d_w_gate_up [E,2I,H] (gate rows = dW_gate, up rows = dW_up, in
+ *   w_gate_up's layout), d_w_down [E,H,I].  Weight gradients are accumulated
+ *   in fp32 over the tokens and stored in grad_dtype; an expert with no slots
+ *   gets exact zeros.  `saved` is the buffer moe_fwd filled for the same
+ *   inputs, or NULL (then Z is recomputed). */
+moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden,
+                     const int32_t* topk_ids, const float* topk_weights,
+                     const void* w_gate_up, const void* w_down,
+                     const void* d_out, const void* saved, void* d_hidden,
+                     float* d_topk_weights, void* d_w_gate_up, void* d_w_down,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream` and reports MOE_ERR_BAD_EXPERT_ID if the last
+ * routing done in `ws` met an id outside [0,E), else MOE_OK. */
+moe_status_t moe_check_device_status(const void* ws, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_str(moe_status_t status);
+
+/* Kernel timing (instrumentation for benchmarks).  While enabled, every
+ * kernel the library launches is bracketed by two HIP events recorded on the
+ * launch stream (events come from a library-owned pool of `max_launches`
+ * pairs, created on enable; later launches are not timed).  moe_timing_read
+ * synchronises those events and returns, per kernel name, the number of
+ * timed launches and their summed duration; it resets the pool.
+ * Not thread-safe; meant for one benchmarking thread. */
+typedef struct {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} moe_kernel_time_t;
+moe_status_t moe_timing_enable(int32_t max_launches);
+moe_status_t moe_timing_disable(void);
+moe_status_t moe_timing_read(moe_kernel_time_t* out, int32_t max_entries,
+                             int32_t* n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

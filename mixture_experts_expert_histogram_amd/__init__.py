@@ -1,0 +1,11 @@
+"""Routed mixture-of-experts expert computation on AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI declared in
+``include/moe.h``; this package is its thin Python binding.  ``build`` compiles
+the library in-tree.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, MoeDesc, MoeError, bwd, check_device_status, empty_workspace, fwd, library,
+    make_desc, route, route_workspace_size, status_str, timing_disable, timing_enable, timing_read,
+    workspace_size,
+)

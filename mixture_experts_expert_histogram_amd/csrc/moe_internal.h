@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP translation units of the MoE library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+// Routing kernels process the slots in chunks of ROUTE_CHUNK per workgroup.
+constexpr int ROUTE_THREADS = 256;
+constexpr int ROUTE_CHUNK = 2048;
+constexpr int MAX_E = 1024;
+// M-tile heights for which the routing scan writes a tile prefix table.
+constexpr int N_TILE_BM = 4;              // 32, 64, 128, 256
+__host__ __device__ constexpr int tile_bm(int j) { return 32 << j; }
+
+// Device views of the routing state that lives in the workspace.
+struct RouteState {
+  int32_t* status;        // [4]  status[0] = number of slots with a bad id
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* tile_prefix;   // [N_TILE_BM][E+1]
+  int32_t* expert_order;  // [E] experts by descending count (ties: lower id)
+  int32_t* blk_hist;      // [nblk][E] (histogram, then per-block base)
+  int32_t* blk_bad;       // [nblk]
+  int32_t* sorted_slot;   // [S]
+  int32_t* inv_pos;       // [S]
+  int32_t* tok_of_pos;    // [S] token of the slot at each position
+  float* w_of_pos;        // [S] routing weight of the slot at each position
+  int nblk;
+};
+
+// Host side: optional timing events around each kernel launch (api.cpp).
+int timing_begin(const char* name, hipStream_t stream);   // slot, or -1 when not timing
+void timing_end(int slot, hipStream_t stream);
+
+template <class F>
+inline hipError_t run_kernel(const char* name, hipStream_t stream, F&& launch) {
+  int slot = timing_begin(name, stream);
+  launch();
+  hipError_t e = hipGetLastError();
+  timing_end(slot, stream);
+  return e;
+}
+
+// ---- routing / combine / reduce (route.hip)
+hipError_t launch_route(const int32_t* ids, const float* w, int S, int K, int E,
+                        const RouteState& rs, hipStream_t stream);
+// out[t] = sum_k Yp[inv_pos[t*K+k]] from fp32 rows, stored in dtype
+hipError_t launch_combine(int dtype, const float* Yp, const int32_t* inv_pos, int T, int K, int H,
+                          void* out, hipStream_t stream);
+hipError_t launch_topkw_reduce(const float* partials, int nparts, const int32_t* inv_pos, int S,
+                               float* dw, hipStream_t stream);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+// ---- grouped GEMMs (gemm.hip)
+struct GemmProblem {
+  int dtype;             // activations / weights: 0 bf16, 1 fp32
+  int gdtype;            // weight gradients: 0 bf16, 1 fp32
+  int act;               // 0 swiglu, 1 clamped
+  int layout;            // 0 concat, 1 interleaved
+  float limit, alpha;
+  int T, H, I, E, K, S;
+  const RouteState* rs;
+};
+// Per-slot buffers are indexed by the expert-sorted position p.
+// forward gate_up projection + GLU: writes a [S,I] (dtype, if a_out) and Z fp32 [S,2I] (if z_out)
+hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
+                          hipStream_t stream);
+// forward down projection with routing weight: Yp fp32 [S,H]
+hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t stream);
+// backward: r = dY.Wd, GLU backward (Z fp32) -> dZ [S,2I], aw = w*a [S,I], partials fp32 [S, nparts]
+hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z,
+                             void* dZ, void* aw, float* partials, int* nparts, hipStream_t stream);
+int down_dgrad_nparts(int I);
+// backward: dXp = dZ . Wgu, fp32 [S,H]
+hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp,
+                                hipStream_t stream);
+// backward weight gradients
+hipError_t launch_wgrad_down(const GemmProblem& pb, const void* dY, const void* aw, void* dWd,
+                             hipStream_t stream);
+hipError_t launch_wgrad_gate_up(const GemmProblem& pb, const void* dZ, const void* X, void* dWgu,
+                                hipStream_t stream);
+
+}  // namespace moe

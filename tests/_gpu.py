@@ -1,0 +1,84 @@
+"""Helpers of the GPU parity tests: device inputs and the comparison bar.
+
+Bar for floating-point outputs (per tensor): relative Frobenius error
+||gpu - ref|| / ||ref|| <= 1e-2 and max |gpu - ref| <= 3e-2 * rms(ref).
+Integer routing outputs must be equal.
+"""
+import numpy as np
+import torch
+
+import oracle
+from synth import HostInputs, Workload, make_host_inputs, to_device
+
+REL_TOL = 1e-2
+MAX_TOL = 3e-2
+
+
+def parity_stats(gpu, ref):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    fro = np.linalg.norm(r)
+    diff = np.linalg.norm(g - r)
+    rms = fro / np.sqrt(max(r.size, 1))
+    mx = float(np.max(np.abs(g - r))) if r.size else 0.0
+    return (diff / fro if fro > 0 else diff), mx, rms
+
+
+BF16_HALF_ULP = 2.0 ** -8   # |bf16(x) - x| <= 2^-8 |x| under round-to-nearest-even
+
+
+def assert_parity(gpu, ref, name, rel_tol=REL_TOL, max_tol=MAX_TOL, stored_bf16=False):
+    """The bar above.  stored_bf16: the tensor is an fp32 sum stored in bf16 by
+    choice of the caller; the rounding of the exact result itself (up to
+    2^-8 |ref| per element) is then added to the max-abs allowance."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    rel, mx, rms = parity_stats(g, r)
+    if rms == 0:
+        assert np.all(g == 0), f"{name}: expected exact zeros"
+        return rel
+    assert rel <= rel_tol, f"{name}: rel-Frobenius {rel:.3e} > {rel_tol}"
+    if stored_bf16:
+        excess = float(np.max(np.abs(g - r) - BF16_HALF_ULP * np.abs(r)))
+        assert excess <= max_tol * rms, f"{name}: max-abs beyond storage rounding {excess:.3e} > {max_tol} * rms {rms:.3e}"
+    else:
+        assert mx <= max_tol * rms, f"{name}: max-abs {mx:.3e} > {max_tol} * rms {rms:.3e}"
+    return rel
+
+
+def host(t):
+    return t.detach().float().cpu().numpy()
+
+
+def device_inputs(inp: HostInputs, dev="cuda"):
+    wl = inp.wl
+    return dict(
+        hidden=to_device(inp.hidden, wl, dev),
+        topk_ids=torch.from_numpy(inp.topk_ids).to(dev),
+        topk_weights=torch.from_numpy(inp.topk_weights).to(dev),
+        w_gate_up=to_device(inp.w_gate_up, wl, dev),
+        w_down=to_device(inp.w_down, wl, dev),
+        d_out=to_device(inp.dout, wl, dev),
+    )
+
+
+def small_inputs(T, H, I, E, K, dtype, act, layout, seed=0, ids=None, xscale=1.0):
+    wl = Workload("case", T, H, I, E, K, dtype, act, layout)
+    inp = make_host_inputs(wl, seed)
+    if ids is not None:
+        inp.topk_ids = np.ascontiguousarray(ids, dtype=np.int32)
+    if xscale != 1.0:
+        from synth import round_to_dtype
+        inp.hidden = round_to_dtype(inp.hidden * xscale, dtype)
+    return inp
+
+
+def oracle_fwd_bwd(inp: HostInputs):
+    wl = inp.wl
+    ex = oracle.expert_accessor(inp.w_gate_up, inp.w_down)
+    out = oracle.forward(inp.hidden, inp.topk_ids, inp.topk_weights, ex, wl.E, wl.act, wl.layout, wl.limit, wl.alpha)
+    grads = oracle.backward(inp.hidden, inp.topk_ids, inp.topk_weights, inp.dout, ex, wl.E, wl.act, wl.layout,
+                            wl.limit, wl.alpha)
+    return out, grads

@@ -1,0 +1,149 @@
+"""GPU parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small cases span several 128-row and 128-column tiles with ragged tails in
+every dimension (H and I not multiples of 64, experts with more than two
+M-tiles, empty experts); bf16 and fp32; SwiGLU and the clamped GLU;
+concatenated and interleaved gate/up rows; saved and recomputed Z.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_expert_histogram_amd as moe
+import oracle
+from synth import WORKLOADS, make_host_inputs, make_routing
+from tests._gpu import assert_parity, device_inputs, host, oracle_fwd_bwd, small_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def skewed_ids(T, K, E, seed):
+    """Expert 0 gets ~40% of slots (several M-tiles), expert E-1 none."""
+    rng = np.random.default_rng(seed)
+    ids = np.where(rng.random((T, K)) < 0.4, 0, rng.integers(1, E - 1, size=(T, K)))
+    return ids.astype(np.int32)
+
+
+def gate_up_halves(x, layout):
+    """(gate rows, up rows) of one expert's [2I, H] block."""
+    I = x.shape[0] // 2
+    return (x[0::2], x[1::2]) if layout == "interleaved" else (x[:I], x[I:])
+
+
+def check_weight_grads(dgu, dd, r_dgu, r_dd, counts, layout, experts=None):
+    """Each expert's dW_gate, dW_up and dW_down is a parameter tensor of its own
+    and meets the bar on its own scale; an expert with no slots gets zeros."""
+    experts = range(len(counts)) if experts is None else experts
+    bf = dgu.dtype == torch.bfloat16
+    for e in experts:
+        g_gu, g_d = host(dgu[e]), host(dd[e])
+        if counts[e] == 0:
+            assert np.all(g_gu == 0) and np.all(g_d == 0), f"expert {e} has no slots but nonzero dW"
+            continue
+        for half, (g, r) in zip(["gate", "up"], zip(gate_up_halves(g_gu, layout), gate_up_halves(r_dgu[e], layout))):
+            assert_parity(g, r, f"dW_{half}[{e}]", stored_bf16=bf)
+        assert_parity(g_d, r_dd[e], f"dW_down[{e}]", stored_bf16=bf)
+
+
+def run_and_compare(inp, save=True, grad_dtype=None):
+    wl = inp.wl
+    d = device_inputs(inp)
+    kw = dict(act=wl.act, layout=wl.layout, limit=wl.limit, alpha=wl.alpha)
+    out, saved, ws = moe.fwd(d["hidden"], d["topk_ids"], d["topk_weights"], d["w_gate_up"], d["w_down"],
+                             save=save, **kw)
+    dh, dw, dgu, dd, ws2 = moe.bwd(d["hidden"], d["topk_ids"], d["topk_weights"], d["w_gate_up"], d["w_down"],
+                                   d["d_out"], saved=saved, grad_dtype=grad_dtype, **kw)
+    torch.cuda.synchronize()
+    assert moe.check_device_status(ws) == 0 and moe.check_device_status(ws2) == 0
+    ref_out, (r_dx, r_dw, r_dgu, r_dd) = oracle_fwd_bwd(inp)
+    assert_parity(host(out), ref_out, "out")
+    assert_parity(host(dh), r_dx, "d_hidden")
+    assert_parity(host(dw), r_dw, "d_topk_weights")
+    # stacked weight gradients: relative Frobenius error over all experts
+    assert_parity(host(dgu), r_dgu, "d_w_gate_up", max_tol=np.inf)
+    assert_parity(host(dd), r_dd, "d_w_down", max_tol=np.inf)
+    check_weight_grads(dgu, dd, r_dgu, r_dd, np.bincount(inp.topk_ids.ravel(), minlength=wl.E), wl.layout)
+    return out, dh, dw, dgu, dd
+
+
+# ------------------------------------------------------------------ routing
+def check_route(ids, E):
+    t = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    counts, offsets, ss, ip, ws = moe.route(t, E)
+    torch.cuda.synchronize()
+    c, o, s, i = oracle.route(ids, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), o)
+    np.testing.assert_array_equal(ss.cpu().numpy(), s)
+    np.testing.assert_array_equal(ip.cpu().numpy(), i)
+    assert moe.check_device_status(ws) == 0
+
+
+@pytest.mark.parametrize("T,K,E,seed", [(1, 1, 1, 0), (7, 3, 5, 1), (1000, 4, 128, 2), (3000, 8, 256, 3),
+                                        (513, 2, 1024, 4), (4096, 4, 3, 5), (257, 64, 17, 6)])
+def test_route_random(T, K, E, seed):
+    check_route(np.random.default_rng(seed).integers(0, E, size=(T, K)), E)
+
+
+def test_route_edge_cases():
+    check_route(np.zeros((5000, 4)), 8)                       # every slot to one expert
+    check_route(np.full((300, 2), 6), 7)                      # only the last expert
+    check_route(skewed_ids(2049, 3, 9, 0), 9)                 # chunk boundary + empty expert
+    ids = np.random.default_rng(1).integers(0, 4, size=(777, 5))
+    ids[:, 1] = ids[:, 0]                                     # duplicates inside each token
+    check_route(ids, 4)
+
+
+@pytest.mark.parametrize("name", ["gptoss", "large", "zipf"])
+def test_route_workloads(name):
+    wl = WORKLOADS[name]
+    ids, _ = make_routing(wl)
+    check_route(ids, wl.E)
+
+
+def test_route_bad_id_sets_flag():
+    ids = np.random.default_rng(2).integers(0, 8, size=(100, 2)).astype(np.int32)
+    ids[10, 1] = 8
+    ids[50, 0] = -3
+    t = torch.from_numpy(ids).cuda()
+    counts, offsets, ss, ip, ws = moe.route(t, 8)
+    assert moe.check_device_status(ws) == 5
+    good = np.ones(200, bool)
+    good[[21, 100]] = False
+    f = ids.ravel()
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(f[good], minlength=8))
+    ipn = ip.cpu().numpy()
+    assert ipn[21] == -1 and ipn[100] == -1
+    # the good slots keep their stable order
+    order = np.argsort(np.where(good, f, 99), kind="stable")[:198]
+    np.testing.assert_array_equal(ss.cpu().numpy()[:198], order)
+
+
+# ------------------------------------------------------------------ fwd + bwd
+def test_tiny_fp32_workload():
+    run_and_compare(make_host_inputs(WORKLOADS["tiny"], seed=0))
+
+
+@pytest.mark.parametrize("act,layout", [("swiglu", "concat"), ("swiglu", "interleaved"),
+                                        ("clamped", "interleaved"), ("clamped", "concat")])
+@pytest.mark.parametrize("dtype,grad_dtype", [("bf16", "fp32"), ("bf16", "bf16"), ("fp32", "fp32")])
+def test_small_ragged(act, layout, dtype, grad_dtype):
+    T, H, I, E, K = 300, 328, 200, 6, 3
+    inp = small_inputs(T, H, I, E, K, dtype, act, layout, seed=3, ids=skewed_ids(T, K, E, 3))
+    run_and_compare(inp, grad_dtype=grad_dtype)
+
+
+@pytest.mark.parametrize("save", [True, False])
+def test_saved_and_recomputed_z_agree(save):
+    T, H, I, E, K = 200, 256, 192, 5, 2
+    inp = small_inputs(T, H, I, E, K, "bf16", "swiglu", "concat", seed=4)
+    run_and_compare(inp, save=save, grad_dtype="fp32")
+
+
+def test_clamps_exercised():
+    T, H, I, E, K = 256, 136, 72, 4, 2
+    inp = small_inputs(T, H, I, E, K, "bf16", "clamped", "interleaved", seed=5, xscale=30.0)
+    z = np.stack([inp.hidden[s // K] @ inp.w_gate_up[inp.topk_ids.ravel()[s]].T.astype(np.float64)
+                  for s in range(T * K)])
+    assert np.mean(np.abs(z) > 7) > 0.05
+    run_and_compare(inp, grad_dtype="fp32")
