@@ -1,0 +1,248 @@
+"""Benchmark of the routed MoE expert computation on one MI355X.
+
+A step is one forward (moe_fwd, keeping Z for the backward) plus one backward
+(moe_bwd) of a routed MoE layer over one batch of synthetic tokens: routing
+permutation, gate_up projection with the gated activation, down projection
+with the routing weight, per-token combine, then the backward's input
+gradients, routing-weight gradients and weight gradients.
+
+Prints one JSON line.  `value` is useful routed TFLOP/s over the whole step:
+forward 6*S*H*I plus backward 12*S*H*I floating-point operations (S = T*K),
+with inputs and weights resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+METRIC = "ms/layer and routed TFLOP/s (fwd, bwd) at 1 MI355X; % of bf16 MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="gptoss", help="synthetic workload name (synth.WORKLOADS)")
+    p.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle's CPU sample")
+    p.add_argument("--no-kernel-timing", action="store_true")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ per-kernel model
+def kernel_model(wl, counts, grad_bytes):
+    """Algorithmic bytes and flops of one launch of each kernel.
+
+    Bytes count each distinct input element read once and each output element
+    written once; only experts that receive slots have their weights read.
+    """
+    S, T, H, I = wl.S, wl.T, wl.H, wl.I
+    eb = 2 if wl.dtype == "bf16" else 4
+    touched = int((counts > 0).sum())
+    Wgu = touched * 2 * I * H * eb
+    Wd = touched * H * I * eb
+    m = {
+        "gate_up_glu": (Wgu + T * H * eb + S * I * eb + S * 2 * I * 4, 4.0 * S * H * I),
+        "down_weighted": (Wd + S * I * eb + S * H * 4 + S * 4, 2.0 * S * H * I),
+        "combine": (S * H * 4 + T * H * eb + S * 4, 0.0),
+        "down_dgrad_glu_bwd": (Wd + T * H * eb + S * 2 * I * 4 + S * 2 * I * eb + S * I * eb, 2.0 * S * H * I),
+        "gate_up_dgrad": (Wgu + S * 2 * I * eb + S * H * 4, 4.0 * S * H * I),
+        "wgrad_down": (T * H * eb + S * I * eb + wl.E * H * I * grad_bytes, 2.0 * S * H * I),
+        "wgrad_gate_up": (S * 2 * I * eb + T * H * eb + wl.E * 2 * I * H * grad_bytes, 4.0 * S * H * I),
+        "topkw_reduce": (S * 4 * 2, 0.0),
+    }
+    return m
+
+
+def roofline_for(name, avg_ms, model):
+    nbytes, flops = model[name]
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        ach = flops / (avg_ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(avg_ms, 4), "algorithmic_bytes": nbytes, "flops": flops}
+    ach = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None, "avg_ms": round(avg_ms, 4),
+            "algorithmic_bytes": nbytes, "flops": flops}
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(wl, ids, w, X, dY, Wgu_dev, Wd_dev, budget_s):
+    """The fp64 oracle on a bounded sample: whole experts of this workload,
+    forward + backward, one expert after another until the budget is spent."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    counts = np.bincount(ids.ravel(), minlength=wl.E)
+    order = [e for e in np.argsort(-counts, kind="stable") if counts[e] > 0]
+    rng = np.random.default_rng(0)
+    order = list(rng.permutation(order))
+    flat_ids, flat_w = ids.ravel(), w.ravel()
+    done_slots, elapsed, experts = 0, 0.0, 0
+    for e in order:
+        slots = np.nonzero(flat_ids == e)[0]
+        tok = slots // wl.K
+        gu = Wgu_dev[e].float().cpu().numpy()
+        dn = Wd_dev[e].float().cpu().numpy()
+        sub_ids = np.zeros((len(slots), 1), dtype=np.int32)
+        sub_w = flat_w[slots].reshape(-1, 1)
+        acc = oracle.expert_accessor(lambda _e: (gu, dn))
+        t0 = time.perf_counter()
+        oracle.forward(X[tok], sub_ids, sub_w, acc, 1, wl.act, wl.layout, wl.limit, wl.alpha)
+        oracle.backward(X[tok], sub_ids, sub_w, dY[tok], acc, 1, wl.act, wl.layout, wl.limit, wl.alpha)
+        elapsed += time.perf_counter() - t0
+        done_slots += len(slots)
+        experts += 1
+        if elapsed >= budget_s:
+            break
+    flops = 18.0 * done_slots * wl.H * wl.I
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{experts} whole experts ({done_slots} slots) of the workload, fp64 forward+backward, "
+                      f"{elapsed:.1f} s", "seconds": round(elapsed, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); "
+              "the expert-parallel multi-GPU path is not part of this library", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_expert_histogram_amd as moe
+    from synth import WORKLOADS, device_weights, make_dout, make_hidden, make_routing, to_device
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {wl}", file=sys.stderr, flush=True)
+    ids_np, w_np = make_routing(wl, seed=0)
+    X_np, dY_np = make_hidden(wl, 0), make_dout(wl, 0)
+    X, dY = to_device(X_np, wl, dev), to_device(dY_np, wl, dev)
+    ids = torch.from_numpy(ids_np).to(dev)
+    w = torch.from_numpy(w_np).to(dev)
+    Wgu, Wd = device_weights(wl, dev, seed=0)
+    kw = dict(act=wl.act, layout=wl.layout, limit=wl.limit, alpha=wl.alpha)
+    gdt = torch.float32 if args.grad_dtype == "fp32" else torch.bfloat16
+    desc = moe.make_desc(wl.T, wl.H, wl.I, wl.E, wl.K, wl.dtype, wl.act, wl.layout, wl.limit, wl.alpha,
+                         args.grad_dtype)
+    fws, bws, sbytes = moe.workspace_size(desc)
+    ws_f = moe.empty_workspace(fws, dev)
+    ws_b = moe.empty_workspace(bws, dev)
+    saved = moe.empty_workspace(sbytes, dev)
+    out = torch.empty_like(X)
+    grads = (torch.empty_like(X), torch.empty((wl.T, wl.K), dtype=torch.float32, device=dev),
+             torch.empty(Wgu.shape, dtype=gdt, device=dev), torch.empty(Wd.shape, dtype=gdt, device=dev))
+    torch.cuda.synchronize()
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    def fwd():
+        moe.fwd(X, ids, w, Wgu, Wd, save=True, ws=ws_f, out=out, saved=saved, **kw)
+
+    def bwd():
+        moe.bwd(X, ids, w, Wgu, Wd, dY, saved=saved, ws=ws_b, grads=grads, grad_dtype=args.grad_dtype, **kw)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if moe.check_device_status(ws_f) != 0:
+        raise RuntimeError("bad expert id reported by the device")
+
+    # separate fwd / bwd timings (context)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms, bwd_ms = [], []
+    for _ in range(max(3, min(args.steps, 10))):
+        ev[0].record(); fwd(); ev[1].record(); bwd(); ev[2].record()
+        torch.cuda.synchronize()
+        fwd_ms.append(ev[0].elapsed_time(ev[1]))
+        bwd_ms.append(ev[1].elapsed_time(ev[2]))
+
+    # timed region: exactly `steps` steps, with per-kernel HIP events on the launch stream
+    timing = not args.no_kernel_timing
+    if timing:
+        moe.timing_enable(64 * args.steps)
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    kernels = {}
+    if timing:
+        kernels = {k: (n, ms) for k, (n, ms) in moe.timing_read().items()}
+        moe.timing_disable()
+    print(f"[bench] {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    S, H, I = wl.S, wl.H, wl.I
+    flops_fwd, flops_bwd = 6.0 * S * H * I, 12.0 * S * H * I
+    value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
+    counts = np.bincount(ids_np.ravel(), minlength=wl.E)
+    model = kernel_model(wl, counts, 4 if args.grad_dtype == "fp32" else 2)
+    roof = None
+    kern_avg = {}
+    if kernels:
+        kern_avg = {k: round(ms / n, 4) for k, (n, ms) in kernels.items()}
+        dominant = max((k for k in kernels if k in model), key=lambda k: kernels[k][1])
+        roof = roofline_for(dominant, kernels[dominant][1] / kernels[dominant][0], model)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, ids_np, w_np, X_np, dY_np, Wgu, Wd, args.cpu_seconds)
+
+    fm, bm = float(np.median(fwd_ms)), float(np.median(bwd_ms))
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: routed MoE layer forward+backward, T={wl.T} H={wl.H} I={wl.I} "
+                               f"E={wl.E} top-{wl.K}, {wl.act} GLU, gate/up {wl.layout}, "
+                               f"{wl.routing} routing, {args.grad_dtype} weight grads, saved Z",
+                   "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K, "parallelism": "single GPU"},
+        "fwd_ms": round(fm, 4),
+        "bwd_ms": round(bm, 4),
+        "fwd_tflops": round(flops_fwd / (fm * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(flops_bwd / (bm * 1e-3) / 1e12, 2),
+        "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roof,
+        "kernels_avg_ms": kern_avg,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
