@@ -275,6 +275,31 @@ hipError_t launch_topkw_reduce(const float* partials, int nparts, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
+// Gather token rows into expert-sorted order: dst[p] = src[tok_of_pos[p]].
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ src,
+                                                          const int32_t* __restrict__ tok, int S, int chunks,
+                                                          uint4* __restrict__ dst) {
+  const long total = (long)S * chunks;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (long)gridDim.x * blockDim.x) {
+    const int p = (int)(idx / chunks);
+    const int c = (int)(idx - (long)p * chunks);
+    dst[idx] = src[(long)tok[p] * chunks + c];
+  }
+}
+
+hipError_t launch_gather_rows(const void* src, const int32_t* tok_of_pos, int S, size_t row_bytes, void* dst,
+                              hipStream_t stream) {
+  if (S == 0) return hipSuccess;
+  const int chunks = (int)(row_bytes / 16);
+  const long total = (long)S * chunks;
+  const long blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  return run_kernel("gather_rows", stream, [&] {
+    gather_rows_kernel<<<grid, 256, 0, stream>>>((const uint4*)src, tok_of_pos, S, chunks, (uint4*)dst);
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Zero fill with vector stores (used instead of a memset so the calls stay
 // capturable as plain kernel nodes).
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, long n16, uint8_t* __restrict__ tail,
