@@ -233,10 +233,6 @@ struct Args {
   const int32_t* offsets;       // [E+1]
   const int32_t* tile_prefix;   // [E+1] M-tiles of 128 rows per expert
   const int32_t* expert_order;  // [E] by descending count
-  // LDS copies of the three routing tables (set by the kernel on entry)
-  const __attribute__((address_space(3))) int32_t* l_offsets;
-  const __attribute__((address_space(3))) int32_t* l_tile_prefix;
-  const __attribute__((address_space(3))) int32_t* l_expert_order;
   const float* w_of_pos;        // [S]
   const void* A;
   const void* B;
@@ -249,11 +245,24 @@ struct Args {
   float limit, alpha;
   int ntn, ntm, nparts;
 };
+// Kernel arguments must have one layout on the host and on the device: only
+// global pointers, ints and floats (an LDS pointer is 4 bytes on the device
+// and 8 on the host).
+static_assert(sizeof(Args) == 10 * 8 + 11 * 4 + 4, "Args layout must match between host and device");
+
+// LDS copies of the routing tables, built by each workgroup on entry.
+typedef const __attribute__((address_space(3))) int32_t* lds_i32;
+struct Tabs {
+  lds_i32 offsets;       // [E+1]
+  lds_i32 tile_prefix;   // [E+1]
+  lds_i32 expert_order;  // [E]
+};
 
 // Row-tile (expert, first row, rows) of tile t in the token-row schedule:
 // tiles ordered by expert, then N-tile, then M-tile.
-__device__ __forceinline__ void row_tile(const Args& g, int t, int& e, int& m0, int& rows, int& nt) {
-  const __attribute__((address_space(3))) int32_t* tp = g.l_tile_prefix;
+__device__ __forceinline__ void row_tile(const Args& g, const Tabs& tb, int t, int& e, int& m0, int& rows,
+                                         int& nt) {
+  lds_i32 tp = tb.tile_prefix;
   const int q = t / g.ntn;
   int lo = 0, hi = g.E;
   while (lo < hi) {
@@ -265,8 +274,8 @@ __device__ __forceinline__ void row_tile(const Args& g, int t, int& e, int& m0, 
   const int local = t - tp[e] * g.ntn;
   nt = local / nm;
   const int mt = local - nt * nm;
-  m0 = g.l_offsets[e] + mt * BM;
-  rows = min(BM, g.l_offsets[e + 1] - m0);
+  m0 = tb.offsets[e] + mt * BM;
+  rows = min(BM, tb.offsets[e + 1] - m0);
 }
 
 // ------------------------------------------------------------------ policies
@@ -297,9 +306,9 @@ struct GateUp {
     KOperand a, b;
     int e, m0, rows, nt;
   };
-  __device__ static int total(const Args& g) { return g.l_tile_prefix[g.E] * g.ntn; }
-  __device__ static void setup(const Args& g, int t, Tile& T, int wave, int lane) {
-    row_tile(g, t, T.e, T.m0, T.rows, T.nt);
+  __device__ static int total(const Args& g, const Tabs& tb) { return tb.tile_prefix[g.E] * g.ntn; }
+  __device__ static void setup(const Args& g, const Tabs& tb, int t, Tile& T, int wave, int lane) {
+    row_tile(g, tb, t, T.e, T.m0, T.rows, T.nt);
     const int H = g.H, I = g.I;
     k_rows(T.a, (const uint16_t*)g.A, H, T.m0, T.rows, H, wave, lane);
     const uint16_t* W = (const uint16_t*)g.B + (size_t)T.e * 2 * I * H;
@@ -363,9 +372,9 @@ struct Down {
     KOperand a, b;
     int e, m0, rows, nt;
   };
-  __device__ static int total(const Args& g) { return g.l_tile_prefix[g.E] * g.ntn; }
-  __device__ static void setup(const Args& g, int t, Tile& T, int wave, int lane) {
-    row_tile(g, t, T.e, T.m0, T.rows, T.nt);
+  __device__ static int total(const Args& g, const Tabs& tb) { return tb.tile_prefix[g.E] * g.ntn; }
+  __device__ static void setup(const Args& g, const Tabs& tb, int t, Tile& T, int wave, int lane) {
+    row_tile(g, tb, t, T.e, T.m0, T.rows, T.nt);
     const int H = g.H, I = g.I;
     k_rows(T.a, (const uint16_t*)g.A, I, T.m0, T.rows, I, wave, lane);
     const uint16_t* W = (const uint16_t*)g.B + (size_t)T.e * H * I;
@@ -409,9 +418,9 @@ struct DownDgrad {
     NOperand b;
     int e, m0, rows, nt;
   };
-  __device__ static int total(const Args& g) { return g.l_tile_prefix[g.E] * g.ntn; }
-  __device__ static void setup(const Args& g, int t, Tile& T, int wave, int lane) {
-    row_tile(g, t, T.e, T.m0, T.rows, T.nt);
+  __device__ static int total(const Args& g, const Tabs& tb) { return tb.tile_prefix[g.E] * g.ntn; }
+  __device__ static void setup(const Args& g, const Tabs& tb, int t, Tile& T, int wave, int lane) {
+    row_tile(g, tb, t, T.e, T.m0, T.rows, T.nt);
     const int H = g.H, I = g.I;
     k_rows(T.a, (const uint16_t*)g.A, H, T.m0, T.rows, H, wave, lane);
     const int n0 = T.nt * BN;
@@ -508,9 +517,9 @@ struct GateUpDgrad {
     NOperand b;
     int e, m0, rows, nt;
   };
-  __device__ static int total(const Args& g) { return g.l_tile_prefix[g.E] * g.ntn; }
-  __device__ static void setup(const Args& g, int t, Tile& T, int wave, int lane) {
-    row_tile(g, t, T.e, T.m0, T.rows, T.nt);
+  __device__ static int total(const Args& g, const Tabs& tb) { return tb.tile_prefix[g.E] * g.ntn; }
+  __device__ static void setup(const Args& g, const Tabs& tb, int t, Tile& T, int wave, int lane) {
+    row_tile(g, tb, t, T.e, T.m0, T.rows, T.nt);
     const int H = g.H, I2 = 2 * g.I;
     k_rows(T.a, (const uint16_t*)g.A, I2, T.m0, T.rows, I2, wave, lane);
     const int n0 = T.nt * BN;
@@ -549,14 +558,14 @@ struct Wgrad {
     NOperand a, b;
     int e, cnt, m0, n0;
   };
-  __device__ static int total(const Args& g) { return g.E * g.ntm * g.ntn; }
-  __device__ static void setup(const Args& g, int t, Tile& T, int wave, int lane) {
+  __device__ static int total(const Args& g, const Tabs&) { return g.E * g.ntm * g.ntn; }
+  __device__ static void setup(const Args& g, const Tabs& tb, int t, Tile& T, int wave, int lane) {
     const int per = g.ntm * g.ntn;
     const int er = t / per, tt = t - er * per;
     const int mt = tt / g.ntn, nt = tt - mt * g.ntn;
-    T.e = g.l_expert_order[er];
-    const int off = g.l_offsets[T.e];
-    T.cnt = g.l_offsets[T.e + 1] - off;
+    T.e = tb.expert_order[er];
+    const int off = tb.offsets[T.e];
+    T.cnt = tb.offsets[T.e + 1] - off;
     T.m0 = mt * BM;
     T.n0 = nt * BN;
     const int H = g.H, I = g.I;
@@ -611,8 +620,8 @@ template <bool GU, bool OB> struct Steps<Wgrad<GU, OB>> {
 
 // ------------------------------------------------------------------ the loop
 // Kind-specific parts come from a policy P:
-//   P::total(g)                      number of tiles
-//   P::setup(g, t, tile, wave, lane) operand addressing + epilogue information
+//   P::total(g, tabs)                      number of tiles
+//   P::setup(g, tabs, t, tile, wave, lane) operand addressing + epilogue information
 //   Steps<P>::nk(g, tile)            k-steps of the tile
 //   P::epilogue(g, tile, acc, ...)   fused epilogue and stores
 // One wave-level zero-page DMA per operand load instruction: keeps the number
@@ -638,21 +647,19 @@ __global__ __launch_bounds__(NT) void persistent_kernel(Args g) {
     tab[(g.E + 1) + i] = g.tile_prefix[i];
     if (i < g.E) tab[2 * (g.E + 1) + i] = g.expert_order[i];
   }
-  g.l_offsets = tab;
-  g.l_tile_prefix = tab + (g.E + 1);
-  g.l_expert_order = tab + 2 * (g.E + 1);
+  const Tabs tb = {tab, tab + (g.E + 1), tab + 2 * (g.E + 1)};
   __syncthreads();
-  const int total = P::total(g);
+  const int total = P::total(g, tb);
 
   typename P::Tile it;          // issue-side tile
   int it_i = 0, it_t = sched_tile(0, total), it_k = 0, it_nk = 0;
-  if (it_t >= 0) { P::setup(g, it_t, it, wave, lane); it_nk = Steps<P>::nk(g, it); }
+  if (it_t >= 0) { P::setup(g, tb, it_t, it, wave, lane); it_nk = Steps<P>::nk(g, it); }
   int issued = 0;
   auto issue_next = [&]() {
     while (it_t >= 0 && it_k >= it_nk) {
       it_t = sched_tile(++it_i, total);
       it_k = 0;
-      if (it_t >= 0) { P::setup(g, it_t, it, wave, lane); it_nk = Steps<P>::nk(g, it); }
+      if (it_t >= 0) { P::setup(g, tb, it_t, it, wave, lane); it_nk = Steps<P>::nk(g, it); }
     }
     lds_char* st = lds + (issued % NSTAGE) * STAGE_BYTES;
     if (it_t >= 0) {
@@ -672,7 +679,7 @@ __global__ __launch_bounds__(NT) void persistent_kernel(Args g) {
     const int t = sched_tile(ci, total);
     if (t < 0) break;
     typename P::Tile ct;
-    P::setup(g, t, ct, wave, lane);
+    P::setup(g, tb, t, ct, wave, lane);
     const int nk = Steps<P>::nk(g, ct);
     f32x16 acc[FM][FN];
 #pragma unroll
