@@ -20,6 +20,8 @@
 // and transposed in registers before their LDS store.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -64,17 +66,30 @@ __device__ __forceinline__ float glu_bwd(float g, float u, float da, int act, fl
   return (uc + 1.f) * q;
 }
 
-// Output layout of a 32x32 MFMA accumulator: lane l holds column l%32 and,
-// for register v, row 8*(v/4) + 4*(l/32) + v%4.
-__device__ __forceinline__ int acc_row(int v, int lane) { return ((v >> 2) << 3) + ((lane >> 5) << 2) + (v & 3); }
+// The MFMA is issued with the B fragment first, so it computes the tile
+// transposed: accumulator element (fm, fn, v) of a lane is output row
+// wm*WTM + fm*32 + lane%32 and output column wn*WTN + fn*32 + acc_col4 + v%4,
+// where acc_col4 = 8*(v/4) + 4*(lane/32).  A lane therefore holds 4
+// consecutive columns of one row per register group, and stores are 16 (fp32)
+// or 8 (bf16) bytes wide.
+__device__ __forceinline__ int acc_col4(int vg, int lane) { return (vg << 3) + ((lane >> 5) << 2); }
 
-// Hardware dispatches consecutive workgroups round-robin over the 8 XCDs.
-// Remap so that each XCD walks a contiguous range of logical tiles (tiles
-// that share operands then share that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int b, int nb) {
-  const int per = nb >> 3;
-  if (b >= (per << 3)) return b;
-  return (b & 7) * per + (b >> 3);
+template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  *(uint2*)p = make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+}
+template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+// interleaved pairs (g0 u0 g1 u1 g2 u2 g3 u3)
+template <typename T> __device__ __forceinline__ void store4x2(T* p, const float* g, const float* u);
+template <> __device__ __forceinline__ void store4x2<uint16_t>(uint16_t* p, const float* g, const float* u) {
+  *(uint4*)p = make_uint4(bf16_bits(g[0]) | (bf16_bits(u[0]) << 16), bf16_bits(g[1]) | (bf16_bits(u[1]) << 16),
+                          bf16_bits(g[2]) | (bf16_bits(u[2]) << 16), bf16_bits(g[3]) | (bf16_bits(u[3]) << 16));
+}
+template <> __device__ __forceinline__ void store4x2<float>(float* p, const float* g, const float* u) {
+  *(float4*)p = make_float4(g[0], u[0], g[1], u[1]);
+  *(float4*)(p + 4) = make_float4(g[2], u[2], g[3], u[3]);
 }
 
 // ------------------------------------------------------------------ config
@@ -107,7 +122,7 @@ struct RowLoader {
   const T* ptr[NI];
   int koff[NI];
   int loff[NI];
-  uint4 reg[NI];
+  uint4 reg[2][NI];   // two register sets: k-steps are fetched two steps ahead
   int kdim;
 
   template <class RowPtr>
@@ -127,18 +142,20 @@ struct RowLoader {
       }
     }
   }
+  template <int SET>
   __device__ __forceinline__ void load(int kt) {
     const int k0 = kt * C::BK;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if (ptr[i] != nullptr && k0 + koff[i] < kdim) reg[i] = *(const uint4*)(ptr[i] + k0);
-      else reg[i] = make_uint4(0, 0, 0, 0);
+      if (ptr[i] != nullptr && k0 + koff[i] < kdim) reg[SET][i] = *(const uint4*)(ptr[i] + k0);
+      else reg[SET][i] = make_uint4(0, 0, 0, 0);
     }
   }
+  template <int SET>
   __device__ __forceinline__ void store(T* lds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      if (ptr[i] != nullptr) *(uint4*)(lds + loff[i]) = reg[i];
+      if (ptr[i] != nullptr) *(uint4*)(lds + loff[i]) = reg[SET][i];
   }
 };
 
@@ -155,7 +172,7 @@ struct TransLoader {
   static constexpr int NI = (ITEMS + C::NT - 1) / C::NT;
   int kb[NI], cb[NI];
   bool on[NI], mn_ok[NI];
-  uint32_t reg[NI][VEC][4];
+  uint32_t reg[2][NI][VEC][4];   // two register sets (see RowLoader)
   int kvalid;
 
   __device__ __forceinline__ void init(int mn_valid, int kvalid_) {
@@ -171,7 +188,7 @@ struct TransLoader {
     }
   }
   // krow(k) -> pointer to element (k, first column of the tile)
-  template <class KRow>
+  template <int SET, class KRow>
   __device__ __forceinline__ void load(int kt, KRow krow) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -180,13 +197,14 @@ struct TransLoader {
         const int k = kt * C::BK + kb[i] * VEC + j;
         if (mn_ok[i] && k < kvalid) {
           const uint4 v = *(const uint4*)(krow(k) + cb[i] * VEC);
-          reg[i][j][0] = v.x; reg[i][j][1] = v.y; reg[i][j][2] = v.z; reg[i][j][3] = v.w;
+          reg[SET][i][j][0] = v.x; reg[SET][i][j][1] = v.y; reg[SET][i][j][2] = v.z; reg[SET][i][j][3] = v.w;
         } else {
-          reg[i][j][0] = reg[i][j][1] = reg[i][j][2] = reg[i][j][3] = 0u;
+          reg[SET][i][j][0] = reg[SET][i][j][1] = reg[SET][i][j][2] = reg[SET][i][j][3] = 0u;
         }
       }
     }
   }
+  template <int SET>
   __device__ __forceinline__ void store(T* lds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -197,12 +215,12 @@ struct TransLoader {
         if (sizeof(T) == 2) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t a = reg[i][2 * q][c >> 1], b = reg[i][2 * q + 1][c >> 1];
+            const uint32_t a = reg[SET][i][2 * q][c >> 1], b = reg[SET][i][2 * q + 1][c >> 1];
             o[q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = reg[i][q][c];
+          for (int q = 0; q < 4; ++q) o[q] = reg[SET][i][q][c];
         }
         const int row = cb[i] * VEC + c;
         *(uint4*)(lds + C::lds_off(row, kb[i])) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -233,7 +251,7 @@ __device__ __forceinline__ void mma_tile(const typename C::elem* As, const typen
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[fn], a[fm], acc[fm][fn], 0, 0, 0);
     } else {
       float a[C::FM], b[C::FN];
       const int k = kk * 2 + half;
@@ -246,13 +264,55 @@ __device__ __forceinline__ void mma_tile(const typename C::elem* As, const typen
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[fn], a[fm], acc[fm][fn], 0, 0, 0);
     }
   }
 }
 
-// Double-buffered K loop: the next tile's global loads are in flight while
-// the current tile is multiplied; one barrier per step.
+// Double-buffered LDS with two register sets: global loads for k-step kt+2
+// are issued before k-step kt is multiplied, so each load has two steps of
+// MFMA work to land; one barrier per step.  The load functors are called as
+// fn(loader, kt, std::integral_constant<int, SET>{}).
+template <int N> using Set = std::integral_constant<int, N>;
+
+// One register set: the next k-step's loads are in flight while the current
+// one is multiplied (used where two sets would not fit in 256 VGPRs).
+template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
+__device__ __forceinline__ void mainloop_pf1(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
+                                             typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
+  using T = typename C::elem;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  if (nk <= 0) return;
+  T* As0 = lds;
+  T* As1 = lds + C::A_ELEMS;
+  T* Bs0 = lds + 2 * C::A_ELEMS;
+  T* Bs1 = Bs0 + C::B_ELEMS;
+  aload(al, 0, Set<0>{});
+  bload(bl, 0, Set<0>{});
+  al.template store<0>(As0);
+  bl.template store<0>(Bs0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool odd = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      aload(al, kt + 1, Set<0>{});
+      bload(bl, kt + 1, Set<0>{});
+    }
+    mma_tile<C>(odd ? As1 : As0, odd ? Bs1 : Bs0, acc);
+    if (more) {
+      al.template store<0>(odd ? As0 : As1);
+      bl.template store<0>(odd ? Bs0 : Bs1);
+    }
+    __syncthreads();
+  }
+}
+
 template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                          typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
@@ -268,24 +328,40 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
   T* As1 = lds + C::A_ELEMS;
   T* Bs0 = lds + 2 * C::A_ELEMS;
   T* Bs1 = Bs0 + C::B_ELEMS;
-  aload(al, 0);
-  bload(bl, 0);
-  al.store(As0);
-  bl.store(Bs0);
+  aload(al, 0, Set<0>{});
+  bload(bl, 0, Set<0>{});
+  if (nk > 1) {
+    aload(al, 1, Set<1>{});
+    bload(bl, 1, Set<1>{});
+  }
+  al.template store<0>(As0);
+  bl.template store<0>(Bs0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool odd = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      aload(al, kt + 1);
-      bload(bl, kt + 1);
+  for (int kt = 0;;) {
+    // even step: LDS buffer 0 holds step kt, register set 1 holds step kt+1
+    if (kt + 2 < nk) {
+      aload(al, kt + 2, Set<0>{});
+      bload(bl, kt + 2, Set<0>{});
     }
-    mma_tile<C>(odd ? As1 : As0, odd ? Bs1 : Bs0, acc);
-    if (more) {
-      al.store(odd ? As0 : As1);
-      bl.store(odd ? Bs0 : Bs1);
+    mma_tile<C>(As0, Bs0, acc);
+    if (kt + 1 < nk) {
+      al.template store<1>(As1);
+      bl.template store<1>(Bs1);
     }
     __syncthreads();
+    if (++kt >= nk) break;
+    // odd step: LDS buffer 1 holds step kt, register set 0 holds step kt+1
+    if (kt + 2 < nk) {
+      aload(al, kt + 2, Set<1>{});
+      bload(bl, kt + 2, Set<1>{});
+    }
+    mma_tile<C>(As1, Bs1, acc);
+    if (kt + 1 < nk) {
+      al.template store<0>(As0);
+      bl.template store<0>(Bs0);
+    }
+    __syncthreads();
+    if (++kt >= nk) break;
   }
 }
 
@@ -308,40 +384,74 @@ struct GArgs {
   int ntn, ntm, nparts;
 };
 
-// Which (expert, first row, rows) an M-tile index maps to; false if past the end.
+// Token-row tiles: (expert, N-tile, M-tile of BM rows), ordered by expert,
+// then N-tile, then M-tile, so the M-tiles of one expert that share a weight
+// tile are neighbours.  The grid is sized for the worst case; the actual tile
+// count is read from the routing tables and split into 8 equal contiguous
+// ranges, one per XCD (hardware deals workgroup b to XCD b % 8).  Returns
+// false for a workgroup without a tile.
 template <int BM>
-__device__ __forceinline__ bool find_mtile(const GArgs& g, int mt, int& e, int& m0, int& rows) {
+__device__ __forceinline__ bool row_tile(const GArgs& g, int& e, int& m0, int& rows, int& nt) {
   const int* tp = g.tile_prefix;
-  if (mt >= tp[g.E]) return false;
-  int lo = 0, hi = g.E;            // largest e with tp[e] <= mt
+  const int ntn = g.ntn;
+  const int total = tp[g.E] * ntn;
+  const int per = (total + 7) >> 3;
+  const int b = blockIdx.x, j = b >> 3;
+  if (j >= per) return false;
+  const int t = (b & 7) * per + j;
+  if (t >= total) return false;
+  const int q = t / ntn;
+  int lo = 0, hi = g.E;            // largest e with tp[e] <= q
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (tp[mid] <= mt) lo = mid; else hi = mid - 1;
+    if (tp[mid] <= q) lo = mid; else hi = mid - 1;
   }
   e = lo;
-  m0 = g.offsets[e] + (mt - tp[e]) * BM;
+  const int nm = tp[e + 1] - tp[e];
+  const int local = t - tp[e] * ntn;
+  nt = local / nm;
+  const int mt = local - nt * nm;
+  m0 = g.offsets[e] + mt * BM;
   rows = min(BM, g.offsets[e + 1] - m0);
   return true;
+}
+
+// Weight-gradient tiles: chunks of 8 consecutive tiles are dealt round-robin
+// to the XCDs in launch order (experts longest first), so every XCD gets a
+// similar share of long and short experts and a chunk's tiles share operands
+// in one L2.  Returns -1 past the end.
+__device__ __forceinline__ int dealt_tile(int total) {
+  const int b = blockIdx.x, x = b & 7, j = b >> 3;
+  const int t = (((j >> 3) << 3) + x) * 8 + (j & 7);
+  return t < total ? t : -1;
 }
 
 #define GEMM_PROLOGUE(C)                                                   \
   using T = typename C::elem;                                              \
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];     \
   T* lds = (T*)smem_raw;                                                   \
-  const int L = xcd_remap(blockIdx.x, gridDim.x);                          \
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;              \
   const int wm = wave / C::WN, wn = wave % C::WN;                          \
   (void)lane; (void)wm; (void)wn;
 
+// bf16 operands fit two register sets in 256 VGPRs; fp32 ones use one.
+template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
+__device__ __forceinline__ void mainloop_rows(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
+                                              typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
+  if constexpr (sizeof(typename C::elem) == 2) mainloop<C>(al, bl, aload, bload, nk, lds, acc);
+  else mainloop_pf1<C>(al, bl, aload, bload, nk, lds, acc);
+}
+
 // ---------------------------------------------------------------- gate_up fwd
-// C[p, n] over local columns n: 32-column groups alternate gate / up for the
-// same activation columns, so every lane holds matching g and u accumulators.
+// Local B rows: 32-row groups alternate gate and up rows of the same 32
+// activation columns, so the fn = 0 and fn = 1 fragments of a wave hold
+// matching g and u values.
 template <class C, bool WRITE_A, bool WRITE_Z>
-__global__ __launch_bounds__(C::NT) void gate_up_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 2) void gate_up_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
-  const int mt = L / g.ntn, nt = L % g.ntn;
-  int e, m0, rows;
-  if (!find_mtile<C::BM>(g, mt, e, m0, rows)) return;
+  static_assert(C::FN == 2 && C::WTN == 64, "gate/up pairing assumes 64-column wave tiles");
+  int e, m0, rows, nt;
+  if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I = g.I;
   const T* X = (const T*)g.A;
   const T* W = (const T*)g.B + (size_t)e * 2 * I * H;
@@ -360,28 +470,38 @@ __global__ __launch_bounds__(C::NT) void gate_up_kernel(GArgs g) {
     return W + (size_t)wrow * H;
   }, H);
   f32x16 acc[C::FM][C::FN];
-  mainloop<C>(al, bl, [](auto& l, int kt) { l.load(kt); }, [](auto& l, int kt) { l.load(kt); },
-              (H + C::BK - 1) / C::BK, lds, acc);
+  mainloop_rows<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
+                   [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
+                   (H + C::BK - 1) / C::BK, lds, acc);
 
   T* a_out = (T*)g.out0;
   float* z_out = (float*)g.out1;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
+    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
+    if (rl >= rows) continue;
+    const size_t p = (size_t)(m0 + rl);
 #pragma unroll
-    for (int c = 0; c < C::FN / 2; ++c) {
-      const int jl = ((wn * C::WTN / 32 + 2 * c) >> 1) * 32 + (lane & 31);
-      const int j = j0 + jl;
+    for (int vg = 0; vg < 4; ++vg) {
+      const int j = j0 + wn * 32 + acc_col4(vg, lane);
+      if (j >= I) continue;
+      float gv[4], uv[4];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = wm * C::WTM + fm * 32 + acc_row(v, lane);
-        if (rl >= rows || j >= I) continue;
-        const size_t p = (size_t)(m0 + rl);
-        const float gv = acc[fm][2 * c][v], uv = acc[fm][2 * c + 1][v];
-        if (WRITE_A) store_val<T>(a_out + p * I + j, glu_fwd(gv, uv, g.act, g.limit, g.alpha));
-        if (WRITE_Z) {
-          const int gcol = layout ? 2 * j : j, ucol = layout ? 2 * j + 1 : I + j;
-          z_out[p * 2 * I + gcol] = gv;
-          z_out[p * 2 * I + ucol] = uv;
+      for (int i = 0; i < 4; ++i) {
+        gv[i] = acc[fm][0][vg * 4 + i];
+        uv[i] = acc[fm][1][vg * 4 + i];
+      }
+      if (WRITE_A)
+        store4<T>(a_out + p * I + j, glu_fwd(gv[0], uv[0], g.act, g.limit, g.alpha),
+                  glu_fwd(gv[1], uv[1], g.act, g.limit, g.alpha), glu_fwd(gv[2], uv[2], g.act, g.limit, g.alpha),
+                  glu_fwd(gv[3], uv[3], g.act, g.limit, g.alpha));
+      if (WRITE_Z) {
+        float* zr = z_out + p * 2 * I;
+        if (layout) {
+          store4x2<float>(zr + 2 * j, gv, uv);
+        } else {
+          store4<float>(zr + j, gv[0], gv[1], gv[2], gv[3]);
+          store4<float>(zr + I + j, uv[0], uv[1], uv[2], uv[3]);
         }
       }
     }
@@ -390,11 +510,10 @@ __global__ __launch_bounds__(C::NT) void gate_up_kernel(GArgs g) {
 
 // ---------------------------------------------------------------- down fwd
 template <class C>
-__global__ __launch_bounds__(C::NT) void down_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 2) void down_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
-  const int mt = L / g.ntn, nt = L % g.ntn;
-  int e, m0, rows;
-  if (!find_mtile<C::BM>(g, mt, e, m0, rows)) return;
+  int e, m0, rows, nt;
+  if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I = g.I;
   const T* Aa = (const T*)g.A;
   const T* W = (const T*)g.B + (size_t)e * H * I;
@@ -404,23 +523,25 @@ __global__ __launch_bounds__(C::NT) void down_kernel(GArgs g) {
   al.init([&](int r) { return Aa + (size_t)(m0 + min(r, rows - 1)) * I; }, I);
   bl.init([&](int r) { return W + (size_t)min(n0 + r, H - 1) * I; }, I);
   f32x16 acc[C::FM][C::FN];
-  mainloop<C>(al, bl, [](auto& l, int kt) { l.load(kt); }, [](auto& l, int kt) { l.load(kt); },
-              (I + C::BK - 1) / C::BK, lds, acc);
+  mainloop_rows<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
+                   [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
+                   (I + C::BK - 1) / C::BK, lds, acc);
   float* Y = (float*)g.out0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
+    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
+    if (rl >= rows) continue;
+    const size_t p = (size_t)(m0 + rl);
+    const float w = g.w_of_pos[p];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rl = wm * C::WTM + fm * 32 + acc_row(v, lane);
-      if (rl >= rows) continue;
-      const int p = m0 + rl;
-      const float w = g.w_of_pos[p];
+    for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n0 + wn * C::WTN + fn * 32 + (lane & 31);
-        if (n < H) Y[(size_t)p * H + n] = w * acc[fm][fn][v];
+      for (int vg = 0; vg < 4; ++vg) {
+        const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+        if (n < H)
+          store4<float>(Y + p * H + n, w * acc[fm][fn][vg * 4], w * acc[fm][fn][vg * 4 + 1],
+                        w * acc[fm][fn][vg * 4 + 2], w * acc[fm][fn][vg * 4 + 3]);
       }
-    }
   }
 }
 
@@ -428,11 +549,10 @@ __global__ __launch_bounds__(C::NT) void down_kernel(GArgs g) {
 // r[p, i] = sum_h dY[tok(p), h] * Wd[e][h, i]; epilogue: a = phi(Z), partial
 // <r, a> per row for dTopkW, da = w r, dZ = phi'(Z) da, aw = w a.
 template <class C>
-__global__ __launch_bounds__(C::NT) void down_dgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
-  const int mt = L / g.ntn, nt = L % g.ntn;
-  int e, m0, rows;
-  if (!find_mtile<C::BM>(g, mt, e, m0, rows)) return;
+  int e, m0, rows, nt;
+  if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I = g.I;
   const T* dY = (const T*)g.A;
   const T* W = (const T*)g.B + (size_t)e * H * I;
@@ -443,55 +563,61 @@ __global__ __launch_bounds__(C::NT) void down_dgrad_kernel(GArgs g) {
   al.init([&](int r) { return dY + (size_t)tok[m0 + min(r, rows - 1)] * H; }, H);
   bl.init(I - n0, H);
   f32x16 acc[C::FM][C::FN];
-  mainloop<C>(al, bl, [](auto& l, int kt) { l.load(kt); },
-              [&](auto& l, int kt) { l.load(kt, [&](int k) { return W + (size_t)k * I + n0; }); },
-              (H + C::BK - 1) / C::BK, lds, acc);
+  mainloop_pf1<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
+                  [&](auto& l, int kt, auto set) {
+                    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * I + n0; });
+                  },
+                  (H + C::BK - 1) / C::BK, lds, acc);
 
   const float* Z = (const float*)g.Z;
   T* dZ = (T*)g.out0;
   T* aw = (T*)g.out1;
   const int layout = g.layout;
-  float rowsum[C::FM][16];
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      rowsum[fm][v] = 0.f;
-      const int rl = wm * C::WTM + fm * 32 + acc_row(v, lane);
-      if (rl >= rows) continue;
-      const size_t p = (size_t)(m0 + rl);
-      const float w = g.w_of_pos[p];
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int i = n0 + wn * C::WTN + fn * 32 + (lane & 31);
-        if (i >= I) continue;
-        const int gcol = layout ? 2 * i : i, ucol = layout ? 2 * i + 1 : I + i;
-        const float gv = Z[p * 2 * I + gcol], uv = Z[p * 2 * I + ucol];
-        const float r = acc[fm][fn][v];
-        float dg, du;
-        const float a = glu_bwd(gv, uv, w * r, g.act, g.limit, g.alpha, dg, du);
-        rowsum[fm][v] += r * a;
-        store_val<T>(dZ + p * 2 * I + gcol, dg);
-        store_val<T>(dZ + p * 2 * I + ucol, du);
-        store_val<T>(aw + p * I + i, w * a);
-      }
-    }
-  }
-  // Row sums over this block's columns: across the 32 lanes of a half-wave,
-  // then across the WN waves in wave order (deterministic).
   float* red = (float*)smem_raw;   // [WN][BM]; the K loop ended with a barrier
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
+    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
+    float rs = 0.f;
+    if (rl < rows) {
+      const size_t p = (size_t)(m0 + rl);
+      const float w = g.w_of_pos[p];
+      const float* zr = Z + p * 2 * I;
+      T* dzr = dZ + p * 2 * I;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float s = rowsum[fm][v];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      s += __shfl_xor(s, 16);
-      if ((lane & 31) == 0) red[wn * C::BM + wm * C::WTM + fm * 32 + acc_row(v, lane)] = s;
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int i = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+          if (i >= I) continue;
+          float gv[4], uv[4];
+          if (layout) {
+            const float4 z0 = *(const float4*)(zr + 2 * i), z1 = *(const float4*)(zr + 2 * i + 4);
+            gv[0] = z0.x; uv[0] = z0.y; gv[1] = z0.z; uv[1] = z0.w;
+            gv[2] = z1.x; uv[2] = z1.y; gv[3] = z1.z; uv[3] = z1.w;
+          } else {
+            const float4 zg = *(const float4*)(zr + i), zu = *(const float4*)(zr + I + i);
+            gv[0] = zg.x; gv[1] = zg.y; gv[2] = zg.z; gv[3] = zg.w;
+            uv[0] = zu.x; uv[1] = zu.y; uv[2] = zu.z; uv[3] = zu.w;
+          }
+          float dg[4], du[4], a[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float r = acc[fm][fn][vg * 4 + q];
+            a[q] = glu_bwd(gv[q], uv[q], w * r, g.act, g.limit, g.alpha, dg[q], du[q]);
+            rs += r * a[q];
+          }
+          if (layout) {
+            store4x2<T>(dzr + 2 * i, dg, du);
+          } else {
+            store4<T>(dzr + i, dg[0], dg[1], dg[2], dg[3]);
+            store4<T>(dzr + I + i, du[0], du[1], du[2], du[3]);
+          }
+          store4<T>(aw + p * I + i, w * a[0], w * a[1], w * a[2], w * a[3]);
+        }
     }
+    // this lane and lane^32 hold the two column halves of the same row
+    rs += __shfl_xor(rs, 32);
+    if (lane < 32) red[wn * C::BM + wm * C::WTM + fm * 32 + lane] = rs;
   }
   __syncthreads();
   for (int r = threadIdx.x; r < rows; r += C::NT) {
@@ -504,11 +630,10 @@ __global__ __launch_bounds__(C::NT) void down_dgrad_kernel(GArgs g) {
 // ---------------------------------------------------------------- gate_up dgrad
 // dXp[p, h] = sum_j dZ[p, j] * Wgu[e][j, h]
 template <class C>
-__global__ __launch_bounds__(C::NT) void gate_up_dgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
-  const int mt = L / g.ntn, nt = L % g.ntn;
-  int e, m0, rows;
-  if (!find_mtile<C::BM>(g, mt, e, m0, rows)) return;
+  int e, m0, rows, nt;
+  if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I2 = 2 * g.I;
   const T* dZ = (const T*)g.A;
   const T* W = (const T*)g.B + (size_t)e * I2 * H;
@@ -518,23 +643,26 @@ __global__ __launch_bounds__(C::NT) void gate_up_dgrad_kernel(GArgs g) {
   al.init([&](int r) { return dZ + (size_t)(m0 + min(r, rows - 1)) * I2; }, I2);
   bl.init(H - n0, I2);
   f32x16 acc[C::FM][C::FN];
-  mainloop<C>(al, bl, [](auto& l, int kt) { l.load(kt); },
-              [&](auto& l, int kt) { l.load(kt, [&](int k) { return W + (size_t)k * H + n0; }); },
-              (I2 + C::BK - 1) / C::BK, lds, acc);
+  mainloop_pf1<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
+                  [&](auto& l, int kt, auto set) {
+                    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * H + n0; });
+                  },
+                  (I2 + C::BK - 1) / C::BK, lds, acc);
   float* dXp = (float*)g.out0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
+    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
+    if (rl >= rows) continue;
+    const size_t p = (size_t)(m0 + rl);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rl = wm * C::WTM + fm * 32 + acc_row(v, lane);
-      if (rl >= rows) continue;
-      const size_t p = (size_t)(m0 + rl);
+    for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n0 + wn * C::WTN + fn * 32 + (lane & 31);
-        if (n < H) dXp[p * H + n] = acc[fm][fn][v];
+      for (int vg = 0; vg < 4; ++vg) {
+        const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+        if (n < H)
+          store4<float>(dXp + p * H + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
+                        acc[fm][fn][vg * 4 + 3]);
       }
-    }
   }
 }
 
@@ -543,9 +671,11 @@ __global__ __launch_bounds__(C::NT) void gate_up_dgrad_kernel(GArgs g) {
 // operands are token-major, so both go through the transposing loader.
 // Experts are visited in descending token count (longest first).
 template <class C, bool GATE_UP, typename OutT>
-__global__ __launch_bounds__(C::NT) void wgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 2) void wgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   const int tiles = g.ntm * g.ntn;
+  const int L = dealt_tile(g.E * tiles);
+  if (L < 0) return;
   const int er = L / tiles, tt = L % tiles;
   const int mt = tt / g.ntn, nt = tt % g.ntn;
   const int e = g.expert_order[er];
@@ -561,15 +691,15 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(GArgs g) {
   al.init(M - m0, cnt);
   bl.init(N - n0, cnt);
   f32x16 acc[C::FM][C::FN];
-  mainloop<C>(
+  mainloop_pf1<C>(
       al, bl,
-      [&](auto& l, int kt) {
-        l.load(kt, [&](int k) {
+      [&](auto& l, int kt, auto set) {
+        l.template load<decltype(set)::value>(kt, [&](int k) {
           return GATE_UP ? Ap + (size_t)(off + k) * 2 * I + m0 : Ap + (size_t)tok[off + k] * H + m0;
         });
       },
-      [&](auto& l, int kt) {
-        l.load(kt, [&](int k) {
+      [&](auto& l, int kt, auto set) {
+        l.template load<decltype(set)::value>(kt, [&](int k) {
           return GATE_UP ? Bp + (size_t)tok[off + k] * H + n0 : Bp + (size_t)(off + k) * I + n0;
         });
       },
@@ -577,16 +707,17 @@ __global__ __launch_bounds__(C::NT) void wgrad_kernel(GArgs g) {
   OutT* dW = (OutT*)g.out0 + (size_t)e * M * N;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
+    const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
+    if (m >= M) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * C::WTM + fm * 32 + acc_row(v, lane);
-      if (m >= M) continue;
+    for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n0 + wn * C::WTN + fn * 32 + (lane & 31);
-        if (n < N) store_val<OutT>(dW + (size_t)m * N + n, acc[fm][fn][v]);
+      for (int vg = 0; vg < 4; ++vg) {
+        const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+        if (n < N)
+          store4<OutT>(dW + (size_t)m * N + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1],
+                       acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
       }
-    }
   }
 }
 
@@ -610,6 +741,11 @@ static GArgs base_args(const GemmProblem& pb, int bm) {
 }
 
 static int mtiles_upper(int S, int E, int bm) { return (S + bm - 1) / bm + (E < S ? E : S); }
+// Token-row grids: worst-case tile count, rounded up to 8 plus 8 (see row_tile).
+static long row_grid(const GemmProblem& pb, int bm, int ntn) {
+  const long t = (long)mtiles_upper(pb.S, pb.E, bm) * ntn;
+  return ((t + 7) / 8) * 8 + 8;
+}
 
 template <class C, bool A, bool Z>
 static hipError_t gate_up_impl(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
@@ -617,7 +753,7 @@ static hipError_t gate_up_impl(const GemmProblem& pb, const void* X, const void*
   GArgs g = base_args(pb, C::BM);
   g.A = X; g.B = Wgu; g.out0 = a_out; g.out1 = z_out;
   g.ntn = (pb.I + C::BN / 2 - 1) / (C::BN / 2);
-  const long grid = (long)mtiles_upper(pb.S, pb.E, C::BM) * g.ntn;
+  const long grid = row_grid(pb, C::BM, g.ntn);
   return run_kernel(A ? "gate_up_glu" : "gate_up_z", s, [&] { gate_up_kernel<C, A, Z><<<grid, C::NT, 0, s>>>(g); });
 }
 
@@ -641,7 +777,7 @@ static hipError_t down_impl(const GemmProblem& pb, const void* a, const void* Wd
   GArgs g = base_args(pb, C::BM);
   g.A = a; g.B = Wd; g.out0 = Yp;
   g.ntn = (pb.H + C::BN - 1) / C::BN;
-  const long grid = (long)mtiles_upper(pb.S, pb.E, C::BM) * g.ntn;
+  const long grid = row_grid(pb, C::BM, g.ntn);
   return run_kernel("down_weighted", s, [&] { down_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
@@ -659,7 +795,7 @@ static hipError_t down_dgrad_impl(const GemmProblem& pb, const void* dY, const v
   g.A = dY; g.B = Wd; g.Z = Z; g.out0 = dZ; g.out1 = aw; g.partials = partials;
   g.ntn = (pb.I + C::BN - 1) / C::BN;
   g.nparts = g.ntn;
-  const long grid = (long)mtiles_upper(pb.S, pb.E, C::BM) * g.ntn;
+  const long grid = row_grid(pb, C::BM, g.ntn);
   return run_kernel("down_dgrad_glu_bwd", s, [&] { down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
@@ -677,7 +813,7 @@ static hipError_t gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, cons
   GArgs g = base_args(pb, C::BM);
   g.A = dZ; g.B = Wgu; g.out0 = dXp;
   g.ntn = (pb.H + C::BN - 1) / C::BN;
-  const long grid = (long)mtiles_upper(pb.S, pb.E, C::BM) * g.ntn;
+  const long grid = row_grid(pb, C::BM, g.ntn);
   return run_kernel("gate_up_dgrad", s, [&] { gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
@@ -694,7 +830,8 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
   const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
   g.ntm = (M + C::BM - 1) / C::BM;
   g.ntn = (N + C::BN - 1) / C::BN;
-  const long grid = (long)pb.E * g.ntm * g.ntn;
+  const long total = (long)pb.E * g.ntm * g.ntn;
+  const long grid = ((total + 63) / 64) * 64;   // whole chunks of 8 tiles on each of the 8 XCDs
   return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s,
                     [&] { wgrad_kernel<C, GU, OutT><<<grid, C::NT, 0, s>>>(g); });
 }
