@@ -50,9 +50,9 @@ Layout make_layout(const Dims& d) {
   L.tok_of_pos = take(d.S * sizeof(int32_t));
   L.w_of_pos = take(d.S * sizeof(float));
   L.route_end = o;
-  // hidden rows gathered into expert order (bf16 path)
-  const size_t perm_rows = d.esz == 2 ? (size_t)d.S * d.H * d.esz : 0;
-  L.f_xp = take(perm_rows);
+  // hidden / d_out rows gathered into expert order
+  const size_t perm_rows = (size_t)d.S * d.H * d.esz;
+  L.f_xp = take(0);
   L.f_a = take((size_t)d.S * d.I * d.esz);
   L.f_y = take((size_t)d.S * d.H * sizeof(float));
   L.f_end = o;
@@ -305,16 +305,20 @@ moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* 
     HIP_TRY(launch_wgrad_gate_up_bf16(pb, dz, xp, d_w_gate_up, stream));
     return MOE_OK;
   }
+  void* xp = b + L.b_xp;
+  void* dyp = b + L.b_dyp;
+  HIP_TRY(launch_gather_rows(hidden, rs.tok_of_pos, (int)d.S, d.H * d.esz, xp, stream));
+  HIP_TRY(launch_gather_rows(d_out, rs.tok_of_pos, (int)d.S, d.H * d.esz, dyp, stream));
   if (!zsrc) {
     HIP_TRY(launch_gate_up(pb, hidden, w_gate_up, nullptr, z, stream));
     zsrc = z;
   }
-  HIP_TRY(launch_down_dgrad(pb, d_out, w_down, zsrc, dz, aw, part, &nparts, stream));
+  HIP_TRY(launch_down_dgrad(pb, dyp, w_down, zsrc, dz, aw, part, &nparts, stream));
   HIP_TRY(launch_topkw_reduce(part, nparts, rs.inv_pos, (int)d.S, d_topk_weights, stream));
   HIP_TRY(launch_gate_up_dgrad(pb, dz, w_gate_up, dx, stream));
   HIP_TRY(launch_combine(pb.dtype, dx, rs.inv_pos, (int)d.T, (int)d.K, (int)d.H, d_hidden, stream));
-  HIP_TRY(launch_wgrad_down(pb, d_out, aw, d_w_down, stream));
-  HIP_TRY(launch_wgrad_gate_up(pb, dz, hidden, d_w_gate_up, stream));
+  HIP_TRY(launch_wgrad_down(pb, dyp, aw, d_w_down, stream));
+  HIP_TRY(launch_wgrad_gate_up(pb, dz, xp, d_w_gate_up, stream));
   return MOE_OK;
 }
 

@@ -546,7 +546,7 @@ __global__ __launch_bounds__(C::NT, 2) void down_kernel(GArgs g) {
 }
 
 // ---------------------------------------------------------------- down dgrad
-// r[p, i] = sum_h dY[tok(p), h] * Wd[e][h, i]; epilogue: a = phi(Z), partial
+// r[p, i] = sum_h dYp[p, h] * Wd[e][h, i]; epilogue: a = phi(Z), partial
 // <r, a> per row for dTopkW, da = w r, dZ = phi'(Z) da, aw = w a.
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
@@ -554,13 +554,12 @@ __global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
   int e, m0, rows, nt;
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I = g.I;
-  const T* dY = (const T*)g.A;
+  const T* dYp = (const T*)g.A;    // d_out rows gathered into expert order
   const T* W = (const T*)g.B + (size_t)e * H * I;
   const int n0 = nt * C::BN;
-  const int* tok = g.tok_of_pos;
   RowLoader<C, C::BM, 0> al;
   TransLoader<C, C::BN, C::NT / 2> bl;
-  al.init([&](int r) { return dY + (size_t)tok[m0 + min(r, rows - 1)] * H; }, H);
+  al.init([&](int r) { return dYp + (size_t)(m0 + min(r, rows - 1)) * H; }, H);
   bl.init(I - n0, H);
   f32x16 acc[C::FM][C::FN];
   mainloop_pf1<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
@@ -668,10 +667,12 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
 
 // ---------------------------------------------------------------- weight grads
 // dW[e][m, n] = sum over the expert's positions p of A[p, m] * B[p, n]; both
-// operands are token-major, so both go through the transposing loader.
-// Experts are visited in descending token count (longest first).
+// operands are position-major rows (hidden and d_out pre-gathered into
+// expert order), so both go through the transposing loader.  Experts are
+// visited in descending token count (longest first).  The K loops are short
+// (an expert's tokens), so three workgroups share a CU to hide latency.
 template <class C, bool GATE_UP, typename OutT>
-__global__ __launch_bounds__(C::NT, 2) void wgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 3) void wgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   const int tiles = g.ntm * g.ntn;
   const int L = dealt_tile(g.E * tiles);
@@ -683,9 +684,8 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_kernel(GArgs g) {
   const int H = g.H, I = g.I;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
   const int m0 = mt * C::BM, n0 = nt * C::BN;
-  const int* tok = g.tok_of_pos;
-  const T* Ap = (const T*)g.A;   // GATE_UP: dZ [S,2I]; else dY [T,H] (gathered)
-  const T* Bp = (const T*)g.B;   // GATE_UP: X [T,H] (gathered); else aw [S,I]
+  const T* Ap = (const T*)g.A;   // GATE_UP: dZ [S,2I]; else dYp [S,H]
+  const T* Bp = (const T*)g.B;   // GATE_UP: Xp [S,H]; else aw [S,I]
   TransLoader<C, C::BM, 0> al;
   TransLoader<C, C::BN, C::NT / 2> bl;
   al.init(M - m0, cnt);
@@ -695,12 +695,12 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_kernel(GArgs g) {
       al, bl,
       [&](auto& l, int kt, auto set) {
         l.template load<decltype(set)::value>(kt, [&](int k) {
-          return GATE_UP ? Ap + (size_t)(off + k) * 2 * I + m0 : Ap + (size_t)tok[off + k] * H + m0;
+          return GATE_UP ? Ap + (size_t)(off + k) * 2 * I + m0 : Ap + (size_t)(off + k) * H + m0;
         });
       },
       [&](auto& l, int kt, auto set) {
         l.template load<decltype(set)::value>(kt, [&](int k) {
-          return GATE_UP ? Bp + (size_t)tok[off + k] * H + n0 : Bp + (size_t)(off + k) * I + n0;
+          return GATE_UP ? Bp + (size_t)(off + k) * H + n0 : Bp + (size_t)(off + k) * I + n0;
         });
       },
       (cnt + C::BK - 1) / C::BK, lds, acc);
@@ -724,6 +724,9 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_kernel(GArgs g) {
 // ------------------------------------------------------------------ host side
 using CfgB = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // bf16
 using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
+// weight gradients: half the LDS per workgroup, so three share a CU
+using CfgWB = Cfg<uint16_t, 128, 128, 32, 2, 2>;
+using CfgWF = Cfg<float, 128, 128, 16, 2, 2>;
 
 static constexpr int log2_bm_index(int bm) { return bm == 32 ? 0 : bm == 64 ? 1 : bm == 128 ? 2 : 3; }
 
@@ -839,8 +842,10 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
 template <bool GU>
 static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
   if (pb.dtype == 0)
-    return pb.gdtype == 0 ? wgrad_impl<CfgB, GU, uint16_t>(pb, A, B, dW, s) : wgrad_impl<CfgB, GU, float>(pb, A, B, dW, s);
-  return pb.gdtype == 0 ? wgrad_impl<CfgF, GU, uint16_t>(pb, A, B, dW, s) : wgrad_impl<CfgF, GU, float>(pb, A, B, dW, s);
+    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s)
+                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s);
+  return pb.gdtype == 0 ? wgrad_impl<CfgWF, GU, uint16_t>(pb, A, B, dW, s)
+                        : wgrad_impl<CfgWF, GU, float>(pb, A, B, dW, s);
 }
 
 hipError_t launch_wgrad_down(const GemmProblem& pb, const void* dY, const void* aw, void* dWd, hipStream_t s) {

@@ -69,14 +69,15 @@ hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu,
                           hipStream_t stream);
 // forward down projection with routing weight: Yp fp32 [S,H]
 hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t stream);
-// backward: r = dY.Wd, GLU backward (Z fp32) -> dZ [S,2I], aw = w*a [S,I], partials fp32 [S, nparts]
+// backward: r = dYp.Wd (d_out rows gathered into expert order), GLU backward (Z fp32)
+//   -> dZ [S,2I], aw = w*a [S,I], partials fp32 [S, nparts]
 hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z,
                              void* dZ, void* aw, float* partials, int* nparts, hipStream_t stream);
 int down_dgrad_nparts(int I);
 // backward: dXp = dZ . Wgu, fp32 [S,H]
 hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp,
                                 hipStream_t stream);
-// backward weight gradients
+// backward weight gradients (dYp, Xp: d_out / hidden rows gathered into expert order)
 hipError_t launch_wgrad_down(const GemmProblem& pb, const void* dY, const void* aw, void* dWd,
                              hipStream_t stream);
 hipError_t launch_wgrad_gate_up(const GemmProblem& pb, const void* dZ, const void* X, void* dWgu,
