@@ -212,7 +212,8 @@ def backward(X, topk_ids, topk_weights, dY, experts, E: int, act: str, layout: s
     Returns (d_hidden [T,H], d_topk_weights [T,K], d_w_gate_up [E,2I,H],
     d_w_down [E,H,I]).  With ``dw_sink`` the weight gradients are handed over
     one expert at a time as dw_sink(e, dWgu_e, dWd_e) instead (None, None is
-    returned for them); an expert with no slots gets exact zeros.
+    returned for them); an expert with no slots gets exact zeros (handed to
+    the sink as dw_sink(e, None, None)).
 
     Per expert, with the forward recomputed:
       r   = dY[tok] @ Wd[e]                 grad of the unweighted expert output
@@ -235,10 +236,8 @@ def backward(X, topk_ids, topk_weights, dY, experts, E: int, act: str, layout: s
     for e in range(E):
         R = sorted_slot[offsets[e]:offsets[e + 1]]
         if R.size == 0:
-            if dw_sink is None:
-                continue
-            Wgu, Wd = experts(e)
-            dw_sink(e, np.zeros_like(Wgu), np.zeros_like(Wd))
+            if dw_sink is not None:
+                dw_sink(e, None, None)
             continue
         tok = R // K
         Wgu, Wd = experts(e)

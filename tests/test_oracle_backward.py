@@ -135,7 +135,8 @@ def test_streamed_weight_grads_equal_stacked():
                                            "concat", dw_sink=lambda e, a, b: got.__setitem__(e, (a, b)))
     assert none1 is None and none2 is None and sorted(got) == list(range(5))
     np.testing.assert_array_equal(dX, full[0])
-    for e in range(5):
+    assert got[2] == (None, None) and np.all(full[2][2] == 0) and np.all(full[3][2] == 0)
+    for e in [0, 1, 3, 4]:
         np.testing.assert_array_equal(got[e][0], full[2][e])
         np.testing.assert_array_equal(got[e][1], full[3][e])
 
