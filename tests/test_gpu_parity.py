@@ -30,11 +30,11 @@ def gate_up_halves(x, layout):
     return (x[0::2], x[1::2]) if layout == "interleaved" else (x[:I], x[I:])
 
 
-def check_weight_grads(dgu, dd, r_dgu, r_dd, counts, layout, experts=None):
+def check_weight_grads(dgu, dd, r_dgu, r_dd, counts, layout, experts=None, bf16_workload=True):
     """Each expert's dW_gate, dW_up and dW_down is a parameter tensor of its own
     and meets the bar on its own scale; an expert with no slots gets zeros."""
     experts = range(len(counts)) if experts is None else experts
-    bf = dgu.dtype == torch.bfloat16
+    bf = bf16_workload
     for e in experts:
         g_gu, g_d = host(dgu[e]), host(dd[e])
         if counts[e] == 0:
@@ -56,13 +56,15 @@ def run_and_compare(inp, save=True, grad_dtype=None):
     torch.cuda.synchronize()
     assert moe.check_device_status(ws) == 0 and moe.check_device_status(ws2) == 0
     ref_out, (r_dx, r_dw, r_dgu, r_dd) = oracle_fwd_bwd(inp)
-    assert_parity(host(out), ref_out, "out")
-    assert_parity(host(dh), r_dx, "d_hidden")
-    assert_parity(host(dw), r_dw, "d_topk_weights")
+    bf = wl.dtype == "bf16"
+    assert_parity(host(out), ref_out, "out", stored_bf16=bf)
+    assert_parity(host(dh), r_dx, "d_hidden", stored_bf16=bf)
+    assert_parity(host(dw), r_dw, "d_topk_weights", stored_bf16=bf)
     # stacked weight gradients: relative Frobenius error over all experts
     assert_parity(host(dgu), r_dgu, "d_w_gate_up", max_tol=np.inf)
     assert_parity(host(dd), r_dd, "d_w_down", max_tol=np.inf)
-    check_weight_grads(dgu, dd, r_dgu, r_dd, np.bincount(inp.topk_ids.ravel(), minlength=wl.E), wl.layout)
+    check_weight_grads(dgu, dd, r_dgu, r_dd, np.bincount(inp.topk_ids.ravel(), minlength=wl.E), wl.layout,
+                       bf16_workload=bf)
     return out, dh, dw, dgu, dd
 
 
