@@ -36,7 +36,49 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle's CPU sample")
     p.add_argument("--no-kernel-timing", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, repeated 5 times (the
+    reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_expert_histogram_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 # ------------------------------------------------------------------ per-kernel model
@@ -121,6 +163,9 @@ def cpu_baseline(wl, ids, w, X, dY, Wgu_dev, Wd_dev, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); "
               "the expert-parallel multi-GPU path is not part of this library", file=sys.stderr)
@@ -209,6 +254,7 @@ def main():
         kern_avg = {k: round(ms / n, 4) for k, (n, ms) in kernels.items()}
         dominant = max((k for k in kernels if k in model), key=lambda k: kernels[k][1])
         roof = roofline_for(dominant, kernels[dominant][1] / kernels[dominant][0], model)
+        roof["traffic"] = measured_traffic(dominant, wl.name)
 
     cpu = None
     if not args.no_cpu_baseline:
