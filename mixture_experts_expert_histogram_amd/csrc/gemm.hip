@@ -229,8 +229,83 @@ struct TransLoader {
   }
 };
 
-// ------------------------------------------------------------------ mainloop
+// MN-contiguous operand kept as rows of k in LDS (bf16 only): the tile is
+// [BK k-rows][128 columns], 256-byte rows whose 16-byte chunks are
+// XOR-swizzled by 4*(row%4); fragments are read with ds_read_b64_tr_b16,
+// which hands each lane 4 consecutive k of one column.  The global loads are
+// the same 16-byte chunks the transposing loader reads, without the register
+// transpose.
+template <class C, int ROT>
+struct NLoader {
+  using T = typename C::elem;
+  static_assert(sizeof(T) == 2, "transposing LDS reads are 16-bit");
+  static constexpr int COLS = 128, CPRN = COLS / 8;
+  static constexpr int ITEMS = C::BK * CPRN;
+  static constexpr int NI = (ITEMS + C::NT - 1) / C::NT;
+  int kr[NI], col[NI], loff[NI];
+  bool on[NI], col_ok[NI];
+  uint4 reg[2][NI];
+  int kvalid;
+
+  __device__ __forceinline__ void init(int mn_valid, int kvalid_) {
+    kvalid = kvalid_;
+    const int t = (threadIdx.x + ROT) % C::NT;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = t + i * C::NT;
+      on[i] = q < ITEMS;
+      kr[i] = q / CPRN;
+      const int c = q % CPRN;
+      col[i] = c * 8;
+      col_ok[i] = on[i] && col[i] < mn_valid;
+      loff[i] = kr[i] * COLS + ((c ^ ((kr[i] & 3) << 2)) << 3);
+    }
+  }
+  template <int SET, class KRow>
+  __device__ __forceinline__ void load(int kt, KRow krow) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = kt * C::BK + kr[i];
+      if (col_ok[i] && k < kvalid) reg[SET][i] = *(const uint4*)(krow(k) + col[i]);
+      else reg[SET][i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  template <int SET>
+  __device__ __forceinline__ void store(T* lds) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (on[i]) *(uint4*)(lds + loff[i]) = reg[SET][i];
+  }
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 32 columns x 16 k of an NLoader tile: lane -> column cb + lane%32,
+// k = kk*16 + 8*(lane/32) + 0..7 (the layout of the K-contiguous fragments).
 template <class C>
+__device__ __forceinline__ bf16x8_t frag_n(const typename C::elem* tile, int cb, int kk, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = cb + ((g & 1) << 4) + ((s & 3) << 2);
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  const lds_char* base = (const lds_char*)tile;
+  s16x4_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int krow = kk * 16 + ((g >> 1) << 3) + h * 4 + (s >> 2);
+    const lds_char* p = base + krow * 256 + ((chunk ^ ((krow & 3) << 2)) << 4) + within;
+    r[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  }
+  bf16x8_t out;
+  s16x4_t* o = (s16x4_t*)&out;
+  o[0] = r[0];
+  o[1] = r[1];
+  return out;
+}
+
+// ------------------------------------------------------------------ mainloop
+template <class C, bool A_N = false, bool B_N = false>
 __device__ __forceinline__ void mma_tile(const typename C::elem* As, const typename C::elem* Bs,
                                          f32x16 (&acc)[C::FM][C::FN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -243,10 +318,12 @@ __device__ __forceinline__ void mma_tile(const typename C::elem* As, const typen
       const int chunk = kk * 2 + half;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
-        a[fm] = *(const bf16x8_t*)(As + C::lds_off(wm * C::WTM + fm * 32 + r32, chunk));
+        a[fm] = A_N ? frag_n<C>(As, wm * C::WTM + fm * 32, kk, lane)
+                    : *(const bf16x8_t*)(As + C::lds_off(wm * C::WTM + fm * 32 + r32, chunk));
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
-        b[fn] = *(const bf16x8_t*)(Bs + C::lds_off(wn * C::WTN + fn * 32 + r32, chunk));
+        b[fn] = B_N ? frag_n<C>(Bs, wn * C::WTN + fn * 32, kk, lane)
+                    : *(const bf16x8_t*)(Bs + C::lds_off(wn * C::WTN + fn * 32 + r32, chunk));
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -277,7 +354,7 @@ template <int N> using Set = std::integral_constant<int, N>;
 
 // One register set: the next k-step's loads are in flight while the current
 // one is multiplied (used where two sets would not fit in 256 VGPRs).
-template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
+template <class C, bool A_N = false, bool B_N = false, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop_pf1(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                              typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
   using T = typename C::elem;
@@ -304,7 +381,7 @@ __device__ __forceinline__ void mainloop_pf1(AL& al, BL& bl, ALoadFn aload, BLoa
       aload(al, kt + 1, Set<0>{});
       bload(bl, kt + 1, Set<0>{});
     }
-    mma_tile<C>(odd ? As1 : As0, odd ? Bs1 : Bs0, acc);
+    mma_tile<C, A_N, B_N>(odd ? As1 : As0, odd ? Bs1 : Bs0, acc);
     if (more) {
       al.template store<0>(odd ? As0 : As1);
       bl.template store<0>(odd ? Bs0 : Bs1);
@@ -313,7 +390,7 @@ __device__ __forceinline__ void mainloop_pf1(AL& al, BL& bl, ALoadFn aload, BLoa
   }
 }
 
-template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
+template <class C, bool A_N = false, bool B_N = false, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                          typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
   using T = typename C::elem;
@@ -343,7 +420,7 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
       aload(al, kt + 2, Set<0>{});
       bload(bl, kt + 2, Set<0>{});
     }
-    mma_tile<C>(As0, Bs0, acc);
+    mma_tile<C, A_N, B_N>(As0, Bs0, acc);
     if (kt + 1 < nk) {
       al.template store<1>(As1);
       bl.template store<1>(Bs1);
@@ -355,7 +432,7 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
       aload(al, kt + 2, Set<1>{});
       bload(bl, kt + 2, Set<1>{});
     }
-    mma_tile<C>(As1, Bs1, acc);
+    mma_tile<C, A_N, B_N>(As1, Bs1, acc);
     if (kt + 1 < nk) {
       al.template store<0>(As0);
       bl.template store<0>(Bs0);
@@ -433,6 +510,12 @@ __device__ __forceinline__ int dealt_tile(int total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;              \
   const int wm = wave / C::WN, wn = wave % C::WN;                          \
   (void)lane; (void)wm; (void)wn;
+
+// MN-contiguous operands: rows of k in LDS read with transposing LDS reads for
+// bf16, an in-register transpose for fp32.
+template <class C, int ROT>
+using MNLoader = std::conditional_t<sizeof(typename C::elem) == 2, NLoader<C, ROT>, TransLoader<C, 128, ROT>>;
+template <class C> constexpr bool kNLayout = sizeof(typename C::elem) == 2;
 
 // bf16 operands fit two register sets in 256 VGPRs; fp32 ones use one.
 template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
@@ -558,15 +641,16 @@ __global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
   const T* W = (const T*)g.B + (size_t)e * H * I;
   const int n0 = nt * C::BN;
   RowLoader<C, C::BM, 0> al;
-  TransLoader<C, C::BN, C::NT / 2> bl;
+  MNLoader<C, C::NT / 2> bl;
   al.init([&](int r) { return dYp + (size_t)(m0 + min(r, rows - 1)) * H; }, H);
   bl.init(I - n0, H);
   f32x16 acc[C::FM][C::FN];
-  mainloop_pf1<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
-                  [&](auto& l, int kt, auto set) {
-                    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * I + n0; });
-                  },
-                  (H + C::BK - 1) / C::BK, lds, acc);
+  auto aload = [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); };
+  auto bload = [&](auto& l, int kt, auto set) {
+    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * I + n0; });
+  };
+  if constexpr (kNLayout<C>) mainloop<C, false, true>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
+  else mainloop_pf1<C>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
 
   const float* Z = (const float*)g.Z;
   T* dZ = (T*)g.out0;
@@ -638,15 +722,16 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
   const T* W = (const T*)g.B + (size_t)e * I2 * H;
   const int n0 = nt * C::BN;
   RowLoader<C, C::BM, 0> al;
-  TransLoader<C, C::BN, C::NT / 2> bl;
+  MNLoader<C, C::NT / 2> bl;
   al.init([&](int r) { return dZ + (size_t)(m0 + min(r, rows - 1)) * I2; }, I2);
   bl.init(H - n0, I2);
   f32x16 acc[C::FM][C::FN];
-  mainloop_pf1<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
-                  [&](auto& l, int kt, auto set) {
-                    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * H + n0; });
-                  },
-                  (I2 + C::BK - 1) / C::BK, lds, acc);
+  auto aload = [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); };
+  auto bload = [&](auto& l, int kt, auto set) {
+    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * H + n0; });
+  };
+  if constexpr (kNLayout<C>) mainloop<C, false, true>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
+  else mainloop_pf1<C>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
   float* dXp = (float*)g.out0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
@@ -670,9 +755,9 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
 // operands are position-major rows (hidden and d_out pre-gathered into
 // expert order), so both go through the transposing loader.  Experts are
 // visited in descending token count (longest first).  The K loops are short
-// (an expert's tokens), so three workgroups share a CU to hide latency.
+// (an expert's tokens), so four workgroups share a CU to hide latency.
 template <class C, bool GATE_UP, typename OutT>
-__global__ __launch_bounds__(C::NT, 3) void wgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, 4) void wgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   const int tiles = g.ntm * g.ntn;
   const int L = dealt_tile(g.E * tiles);
@@ -686,24 +771,23 @@ __global__ __launch_bounds__(C::NT, 3) void wgrad_kernel(GArgs g) {
   const int m0 = mt * C::BM, n0 = nt * C::BN;
   const T* Ap = (const T*)g.A;   // GATE_UP: dZ [S,2I]; else dYp [S,H]
   const T* Bp = (const T*)g.B;   // GATE_UP: Xp [S,H]; else aw [S,I]
-  TransLoader<C, C::BM, 0> al;
-  TransLoader<C, C::BN, C::NT / 2> bl;
+  MNLoader<C, 0> al;
+  MNLoader<C, C::NT / 2> bl;
   al.init(M - m0, cnt);
   bl.init(N - n0, cnt);
   f32x16 acc[C::FM][C::FN];
-  mainloop_pf1<C>(
-      al, bl,
-      [&](auto& l, int kt, auto set) {
-        l.template load<decltype(set)::value>(kt, [&](int k) {
-          return GATE_UP ? Ap + (size_t)(off + k) * 2 * I + m0 : Ap + (size_t)(off + k) * H + m0;
-        });
-      },
-      [&](auto& l, int kt, auto set) {
-        l.template load<decltype(set)::value>(kt, [&](int k) {
-          return GATE_UP ? Bp + (size_t)(off + k) * H + n0 : Bp + (size_t)(off + k) * I + n0;
-        });
-      },
-      (cnt + C::BK - 1) / C::BK, lds, acc);
+  auto aload = [&](auto& l, int kt, auto set) {
+    l.template load<decltype(set)::value>(kt, [&](int k) {
+      return GATE_UP ? Ap + (size_t)(off + k) * 2 * I + m0 : Ap + (size_t)(off + k) * H + m0;
+    });
+  };
+  auto bload = [&](auto& l, int kt, auto set) {
+    l.template load<decltype(set)::value>(kt, [&](int k) {
+      return GATE_UP ? Bp + (size_t)(off + k) * H + n0 : Bp + (size_t)(off + k) * I + n0;
+    });
+  };
+  if constexpr (kNLayout<C>) mainloop_pf1<C, true, true>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
+  else mainloop_pf1<C>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
   OutT* dW = (OutT*)g.out0 + (size_t)e * M * N;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
