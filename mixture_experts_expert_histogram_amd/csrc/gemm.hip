@@ -114,15 +114,21 @@ struct Cfg {
 };
 
 // K-contiguous operand: tile rows are m (or n), each row a contiguous run of k.
+// Every load is issued unconditionally (an out-of-range chunk reads its row's
+// first chunk instead) and masked to zero when written to LDS, so the loop
+// body has no branches and the compiler can keep later loads in flight.
 template <class C, int ROWS, int ROT>
 struct RowLoader {
   using T = typename C::elem;
   static constexpr int ITEMS = ROWS * C::CPR;
   static constexpr int NI = (ITEMS + C::NT - 1) / C::NT;
-  const T* ptr[NI];
+  static constexpr bool ALL_ON = ITEMS % C::NT == 0;
+  const T* rowp[NI];
   int koff[NI];
   int loff[NI];
+  bool on[NI];
   uint4 reg[2][NI];   // two register sets: k-steps are fetched two steps ahead
+  bool okm[2][NI];
   int kdim;
 
   template <class RowPtr>
@@ -132,14 +138,12 @@ struct RowLoader {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = t + i * C::NT;
-      if (q < ITEMS) {
-        const int row = q / C::CPR, c = q % C::CPR;
-        ptr[i] = rowptr(row) + c * C::VEC;
-        koff[i] = c * C::VEC;
-        loff[i] = C::lds_off(row, c);
-      } else {
-        ptr[i] = nullptr;
-      }
+      on[i] = ALL_ON || q < ITEMS;
+      const int qq = on[i] ? q : 0;
+      const int row = qq / C::CPR, c = qq % C::CPR;
+      rowp[i] = rowptr(row);
+      koff[i] = c * C::VEC;
+      loff[i] = C::lds_off(row, c);
     }
   }
   template <int SET>
@@ -147,15 +151,16 @@ struct RowLoader {
     const int k0 = kt * C::BK;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if (ptr[i] != nullptr && k0 + koff[i] < kdim) reg[SET][i] = *(const uint4*)(ptr[i] + k0);
-      else reg[SET][i] = make_uint4(0, 0, 0, 0);
+      const bool ok = k0 + koff[i] < kdim;
+      okm[SET][i] = ok;
+      reg[SET][i] = *(const uint4*)(rowp[i] + (ok ? k0 + koff[i] : 0));
     }
   }
   template <int SET>
   __device__ __forceinline__ void store(T* lds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      if (ptr[i] != nullptr) *(uint4*)(lds + loff[i]) = reg[SET][i];
+      if (on[i]) *(uint4*)(lds + loff[i]) = okm[SET][i] ? reg[SET][i] : make_uint4(0, 0, 0, 0);
   }
 };
 
@@ -173,6 +178,7 @@ struct TransLoader {
   int kb[NI], cb[NI];
   bool on[NI], mn_ok[NI];
   uint32_t reg[2][NI][VEC][4];   // two register sets (see RowLoader)
+  bool okm[2][NI][VEC];
   int kvalid;
 
   __device__ __forceinline__ void init(int mn_valid, int kvalid_) {
@@ -194,13 +200,13 @@ struct TransLoader {
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
+        // unconditional load (row 0, column 0 of the tile when out of range;
+        // a tile is only loaded when kvalid >= 1), masked in store()
         const int k = kt * C::BK + kb[i] * VEC + j;
-        if (mn_ok[i] && k < kvalid) {
-          const uint4 v = *(const uint4*)(krow(k) + cb[i] * VEC);
-          reg[SET][i][j][0] = v.x; reg[SET][i][j][1] = v.y; reg[SET][i][j][2] = v.z; reg[SET][i][j][3] = v.w;
-        } else {
-          reg[SET][i][j][0] = reg[SET][i][j][1] = reg[SET][i][j][2] = reg[SET][i][j][3] = 0u;
-        }
+        const bool ok = mn_ok[i] && k < kvalid;
+        okm[SET][i][j] = ok;
+        const uint4 v = *(const uint4*)(krow(ok ? k : 0) + (ok ? cb[i] * VEC : 0));
+        reg[SET][i][j][0] = v.x; reg[SET][i][j][1] = v.y; reg[SET][i][j][2] = v.z; reg[SET][i][j][3] = v.w;
       }
     }
   }
@@ -209,6 +215,9 @@ struct TransLoader {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (!on[i]) continue;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        if (!okm[SET][i][j]) reg[SET][i][j][0] = reg[SET][i][j][1] = reg[SET][i][j][2] = reg[SET][i][j][3] = 0u;
 #pragma unroll
       for (int c = 0; c < VEC; ++c) {
         uint32_t o[4];
@@ -245,6 +254,7 @@ struct NLoader {
   int kr[NI], col[NI], loff[NI];
   bool on[NI], col_ok[NI];
   uint4 reg[2][NI];
+  bool okm[2][NI];
   int kvalid;
 
   __device__ __forceinline__ void init(int mn_valid, int kvalid_) {
@@ -265,16 +275,19 @@ struct NLoader {
   __device__ __forceinline__ void load(int kt, KRow krow) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      // unconditional load (row 0, column 0 of the tile when out of range;
+      // a tile is only loaded when kvalid >= 1), masked in store()
       const int k = kt * C::BK + kr[i];
-      if (col_ok[i] && k < kvalid) reg[SET][i] = *(const uint4*)(krow(k) + col[i]);
-      else reg[SET][i] = make_uint4(0, 0, 0, 0);
+      const bool ok = col_ok[i] && k < kvalid;
+      okm[SET][i] = ok;
+      reg[SET][i] = *(const uint4*)(krow(ok ? k : 0) + (ok ? col[i] : 0));
     }
   }
   template <int SET>
   __device__ __forceinline__ void store(T* lds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      if (on[i]) *(uint4*)(lds + loff[i]) = reg[SET][i];
+      if (on[i]) *(uint4*)(lds + loff[i]) = okm[SET][i] ? reg[SET][i] : make_uint4(0, 0, 0, 0);
   }
 };
 
@@ -405,21 +418,21 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
   T* As1 = lds + C::A_ELEMS;
   T* Bs0 = lds + 2 * C::A_ELEMS;
   T* Bs1 = Bs0 + C::B_ELEMS;
+  // Every prefetch is issued, clamped to the last step (a redundant reload of
+  // a tile that is still in L2), so the number of loads in flight does not
+  // depend on a branch and the LDS stores of one set wait only for that set.
+  const int last = nk - 1;
   aload(al, 0, Set<0>{});
   bload(bl, 0, Set<0>{});
-  if (nk > 1) {
-    aload(al, 1, Set<1>{});
-    bload(bl, 1, Set<1>{});
-  }
+  aload(al, min(1, last), Set<1>{});
+  bload(bl, min(1, last), Set<1>{});
   al.template store<0>(As0);
   bl.template store<0>(Bs0);
   __syncthreads();
   for (int kt = 0;;) {
     // even step: LDS buffer 0 holds step kt, register set 1 holds step kt+1
-    if (kt + 2 < nk) {
-      aload(al, kt + 2, Set<0>{});
-      bload(bl, kt + 2, Set<0>{});
-    }
+    aload(al, min(kt + 2, last), Set<0>{});
+    bload(bl, min(kt + 2, last), Set<0>{});
     mma_tile<C, A_N, B_N>(As0, Bs0, acc);
     if (kt + 1 < nk) {
       al.template store<1>(As1);
@@ -428,10 +441,8 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
     __syncthreads();
     if (++kt >= nk) break;
     // odd step: LDS buffer 1 holds step kt, register set 0 holds step kt+1
-    if (kt + 2 < nk) {
-      aload(al, kt + 2, Set<1>{});
-      bload(bl, kt + 2, Set<1>{});
-    }
+    aload(al, min(kt + 2, last), Set<1>{});
+    bload(bl, min(kt + 2, last), Set<1>{});
     mma_tile<C, A_N, B_N>(As1, Bs1, acc);
     if (kt + 1 < nk) {
       al.template store<0>(As0);
