@@ -49,8 +49,9 @@
  *     from every sum, a flag is set in the workspace, and
  *     moe_check_device_status reports MOE_ERR_BAD_EXPERT_ID; the outputs of
  *     that call are then unspecified.
- *   - T = 0 is valid: nothing is launched for the activations; moe_bwd still
- *     writes zero weight gradients.
+ *   - T = 0 is valid: nothing is launched for the activations; moe_fwd and
+ *     moe_bwd clear the workspace status word (so moe_check_device_status
+ *     reports MOE_OK for the call) and moe_bwd writes zero weight gradients.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

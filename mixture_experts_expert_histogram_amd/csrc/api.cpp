@@ -236,7 +236,10 @@ moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden, const int32_t* 
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
   if (ws_bytes < L.f_end) return MOE_ERR_WORKSPACE;
-  if (d.T == 0) return MOE_OK;
+  if (d.T == 0) {   // nothing to route: clear the status word so it reports this call
+    HIP_TRY(launch_fill_zero((char*)ws + L.status, 4 * sizeof(int32_t), stream));
+    return MOE_OK;
+  }
   RouteState rs = route_state(ws, L, d);
   GemmProblem pb = problem(desc, d, &rs);
   char* b = (char*)ws;
@@ -272,7 +275,8 @@ moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* 
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
   if (ws_bytes < L.b_end) return MOE_ERR_WORKSPACE;
-  if (d.T == 0) {
+  if (d.T == 0) {   // no slots: zero weight gradients, and a status word that reports this call
+    HIP_TRY(launch_fill_zero((char*)ws + L.status, 4 * sizeof(int32_t), stream));
     HIP_TRY(launch_fill_zero(d_w_gate_up, (size_t)d.E * 2 * d.I * d.H * d.gsz, stream));
     HIP_TRY(launch_fill_zero(d_w_down, (size_t)d.E * d.H * d.I * d.gsz, stream));
     return MOE_OK;

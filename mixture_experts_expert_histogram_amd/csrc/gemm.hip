@@ -20,6 +20,7 @@
 // and transposed in registers before their LDS store.
 #include "moe_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
@@ -193,6 +194,12 @@ struct TransLoader {
       mn_ok[i] = on[i] && cb[i] * VEC < mn_valid;
     }
   }
+  // Re-target to a tile with mn_valid columns and kvalid k rows.
+  __device__ __forceinline__ void retarget(int mn_valid, int kvalid_) {
+    kvalid = kvalid_;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) mn_ok[i] = on[i] && cb[i] * VEC < mn_valid;
+  }
   // krow(k) -> pointer to element (k, first column of the tile)
   template <int SET, class KRow>
   __device__ __forceinline__ void load(int kt, KRow krow) {
@@ -270,6 +277,11 @@ struct NLoader {
       col_ok[i] = on[i] && col[i] < mn_valid;
       loff[i] = kr[i] * COLS + ((c ^ ((kr[i] & 3) << 2)) << 3);
     }
+  }
+  __device__ __forceinline__ void retarget(int mn_valid, int kvalid_) {
+    kvalid = kvalid_;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) col_ok[i] = on[i] && col[i] < mn_valid;
   }
   template <int SET, class KRow>
   __device__ __forceinline__ void load(int kt, KRow krow) {
@@ -470,6 +482,7 @@ struct GArgs {
   int act, layout;
   float limit, alpha;
   int ntn, ntm, nparts;
+  int big;   // weight grads: experts with more positions than this are split over the XCDs
 };
 
 // Token-row tiles: (expert, N-tile, M-tile of BM rows), ordered by expert,
@@ -764,63 +777,300 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
 // ---------------------------------------------------------------- weight grads
 // dW[e][m, n] = sum over the expert's positions p of A[p, m] * B[p, n]; both
 // operands are position-major rows (hidden and d_out pre-gathered into
-// expert order), so both go through the transposing loader.  Experts are
-// visited in descending token count (longest first).  The K loops are short
-// (an expert's tokens), so four workgroups share a CU to hide latency.
+// expert order), so both are MN-contiguous.  The output (E x M x N fp32,
+// written once) dominates the traffic and the K loops are short (an expert's
+// positions), so the kernel is built around keeping the store stream busy:
+//
+// * One persistent workgroup per CU with two roles.  Waves 0-3 load operands
+//   and run the MFMAs; waves 4-7 only write dW.  At the end of a tile the MMA
+//   waves put the fp32 accumulators into an LDS staging tile and go on with
+//   the next tile; the store waves copy the staging tile to dW in whole
+//   512-byte row segments.  A wave's vmcnt counts its loads and stores in
+//   issue order, so a wave that did both would wait for its stores before
+//   using later loads; split over two roles, neither stream waits for the
+//   other.
+// * The MMA waves run one pipelined step loop across all of their tiles:
+//   the loads for the step after next (possibly of the next tile) are in
+//   flight while a step is multiplied.
+// * Both roles walk the same (tile, k-step) cursor and meet at the same
+//   barriers: one per step, one more after a finished tile is staged.
+//
+// Tile placement (hardware deals workgroup b to XCD b % 8).  Experts are
+// visited in descending position count.  Experts with at most g.big
+// positions are pinned whole to one XCD, dealt round-robin, so their
+// activations are fetched into one L2 only; larger experts come first and
+// are split into 8 contiguous tile ranges, one per XCD, so skewed routing
+// stays balanced.  An XCD's tile list (split experts' ranges, then its
+// pinned experts) is dealt round-robin to its workgroups, so the workgroups
+// of one XCD work on neighbouring tiles that share operands.
+struct WgradPlan {
+  int tiles, tpx;
+};
+__host__ __device__ inline WgradPlan wgrad_plan(int ntm, int ntn) {
+  WgradPlan p;
+  p.tiles = ntm * ntn;
+  p.tpx = (p.tiles + 7) / 8;
+  return p;
+}
+
+struct WItem {
+  int e, off, cnt, nk, m0, n0;
+};
+
+// The routing tables are copied to LDS at kernel start: lookups from global
+// memory inside the loops would be vector loads (the compiler cannot prove
+// the dW stores do not alias them), and a wave's vmcnt would then make each
+// lookup wait for every load and store the wave has in flight.
+struct WgradTables {
+  int order[MAX_E];
+  int offsets[MAX_E + 1];
+};
+
+template <class C>
+struct WgradList {
+  const WgradTables* tab;   // in LDS
+  int E, ntn, tiles, tpx, nb, x, len_x, count;
+
+  __device__ __forceinline__ void init(const GArgs& g, const WgradTables* t) {
+    tab = t;
+    E = g.E;
+    ntn = g.ntn;
+    const WgradPlan p = wgrad_plan(g.ntm, g.ntn);
+    tiles = p.tiles;
+    tpx = p.tpx;
+    int l = 0, h = E;   // nb = leading experts (descending count) with count > big
+    while (l < h) {
+      const int mid = (l + h) >> 1;
+      const int e = tab->order[mid];
+      if (tab->offsets[e + 1] - tab->offsets[e] > g.big) l = mid + 1; else h = mid;
+    }
+    nb = l;
+    x = blockIdx.x & 7;
+    len_x = max(0, min((x + 1) * tpx, tiles) - x * tpx);
+    const int npin = E - nb - x > 0 ? (E - nb - x + 7) / 8 : 0;
+    count = nb * len_x + npin * tiles;
+  }
+  // Item i (0 <= i < count) of this XCD's list.  An expert without positions
+  // gets one k-step whose loads are all masked (at row 0, which exists: the
+  // kernel only runs with S > 0).
+  __device__ __forceinline__ WItem item(int i) const {
+    int er, t;
+    if (i < nb * len_x) {
+      er = i / len_x;
+      t = x * tpx + (i - er * len_x);
+    } else {
+      i -= nb * len_x;
+      const int q = i / tiles;
+      t = i - q * tiles;
+      er = nb + x + 8 * q;
+    }
+    WItem it;
+    it.e = tab->order[er];
+    it.off = tab->offsets[it.e];
+    it.cnt = tab->offsets[it.e + 1] - it.off;
+    if (it.cnt == 0) it.off = 0;
+    it.nk = max(1, (it.cnt + C::BK - 1) / C::BK);
+    it.m0 = (t / ntn) * C::BM;
+    it.n0 = (t % ntn) * C::BN;
+    return it;
+  }
+};
+
+// Staging tile: [BM rows][BN fp32], 16-byte chunks XOR-swizzled by row.
+template <class C>
+__device__ __forceinline__ int stage_off(int r, int c4) {
+  return r * C::BN + ((c4 ^ (r & 31)) << 2);
+}
+
+constexpr int kStoreThreads = 256;   // four store waves
+
 template <class C, bool GATE_UP, typename OutT>
-__global__ __launch_bounds__(C::NT, 4) void wgrad_kernel(GArgs g) {
-  GEMM_PROLOGUE(C)
-  const int tiles = g.ntm * g.ntn;
-  const int L = dealt_tile(g.E * tiles);
-  if (L < 0) return;
-  const int er = L / tiles, tt = L % tiles;
-  const int mt = tt / g.ntn, nt = tt % g.ntn;
-  const int e = g.expert_order[er];
-  const int off = g.offsets[e], cnt = g.offsets[e + 1] - off;
+__global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g) {
+  using T = typename C::elem;
+  static_assert(C::BN == 128, "store waves copy 32 chunks per row");
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES + C::BM * C::BN * 4];
+  T* lds = (T*)smem_raw;
+  float* stage = (float*)(smem_raw + C::LDS_BYTES);
   const int H = g.H, I = g.I;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
-  const int m0 = mt * C::BM, n0 = nt * C::BN;
-  const T* Ap = (const T*)g.A;   // GATE_UP: dZ [S,2I]; else dYp [S,H]
-  const T* Bp = (const T*)g.B;   // GATE_UP: Xp [S,H]; else aw [S,I]
+  const int lda = M, ldb = N;       // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
+  OutT* dW = (OutT*)g.out0;
+  __shared__ WgradTables tab;
+  for (int i = threadIdx.x; i <= g.E; i += C::NT + kStoreThreads) {
+    if (i < g.E) tab.order[i] = g.expert_order[i];
+    tab.offsets[i] = g.offsets[i];
+  }
+  __syncthreads();
+  WgradList<C> list;
+  list.init(g, &tab);
+  const int K = gridDim.x >> 3;     // workgroups per XCD
+  int ci = blockIdx.x >> 3;         // list item being multiplied / stored
+  if (ci >= list.count) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Steps of this workgroup (one list item per lane, summed over the wave).
+  int total = 0;
+  for (int base = ci; base < list.count; base += 64 * K) {
+    const int i = base + (threadIdx.x & 63) * K;
+    int v = i < list.count ? list.item(i).nk : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    total += v;
+  }
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int total_even = (total + 1) & ~1;   // the MMA loop runs two steps per iteration
+  WItem cur = list.item(ci);
+  int ck = 0;
+  // Advances the multiply cursor (stays on the last step at the end).
+  auto next_step = [&]() {
+    if (ck + 1 < cur.nk) ++ck;
+    else if (ci + K < list.count) { ci += K; cur = list.item(ci); ck = 0; }
+  };
+  if (wave >= C::NT / 64) {
+    // ---------------- store waves
+    // A staged tile is read into registers at once (freeing the staging
+    // tile) and written out a quarter at a time, one quarter per barrier
+    // interval, with any rest flushed before the next tile is read.  Issuing
+    // all of it at once would block the store waves on a saturated write
+    // path and hold up the MMA waves at the next barrier.
+    const int tid = threadIdx.x - C::NT;
+    constexpr int PER = C::BM * 32 / kStoreThreads;
+    constexpr int NQ = 4, QS = PER / NQ;
+    static_assert(PER % NQ == 0, "store quarters");
+    float4 v[PER];
+    OutT* dWt = dW;        // tile origin in dW of the registers' tile
+    int next_q = NQ;       // next quarter to write (NQ: none pending)
+    int stage_rows = 0, stage_cols = 0;
+    auto write_quarter = [&](int q) {
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        if (qq != q) continue;
+#pragma unroll
+        for (int j = 0; j < QS; ++j) {
+          const int i = qq * QS + j;
+          const int idx = tid + i * kStoreThreads;
+          const int r = idx >> 5, c = (idx & 31) * 4;
+          if (r < stage_rows && c < stage_cols)
+            store4<OutT>(dWt + (size_t)r * N + c, v[i].x, v[i].y, v[i].z, v[i].w);
+        }
+      }
+    };
+    __syncthreads();   // prologue
+    for (int st = 0; st < total_even; ++st) {
+      __syncthreads();   // step done
+      if (next_q < NQ) write_quarter(next_q++);
+      if (st < total && ck + 1 == cur.nk) {
+        while (next_q < NQ) write_quarter(next_q++);
+        __syncthreads();   // tile staged
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int idx = tid + i * kStoreThreads;
+          v[i] = *(const float4*)(stage + stage_off<C>(idx >> 5, idx & 31));
+        }
+        dWt = dW + ((size_t)cur.e * M + cur.m0) * N + cur.n0;
+        stage_rows = min(C::BM, M - cur.m0);
+        stage_cols = min(C::BN, N - cur.n0);
+        next_q = 0;
+        write_quarter(next_q++);
+      }
+      next_step();
+    }
+    while (next_q < NQ) write_quarter(next_q++);
+    return;
+  }
+
+  // ---------------- MMA waves
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   MNLoader<C, 0> al;
   MNLoader<C, C::NT / 2> bl;
-  al.init(M - m0, cnt);
-  bl.init(N - n0, cnt);
+  al.init(M - cur.m0, cur.cnt);
+  bl.init(N - cur.n0, cur.cnt);
+  // Load cursor, two steps ahead of the multiply cursor.  It stops at the
+  // last step, so loads past the end re-read that step and every step issues
+  // the same loads.
+  int li = ci, lk = 0;
+  WItem ld = cur;
+  const T* Ag = (const T*)g.A;
+  const T* Bg = (const T*)g.B;
+  auto issue = [&](auto set) {
+    constexpr int SET = decltype(set)::value;
+    al.retarget(M - ld.m0, ld.cnt);
+    bl.retarget(N - ld.n0, ld.cnt);
+    const T* Ap = Ag + (size_t)ld.off * lda + ld.m0;
+    const T* Bp = Bg + (size_t)ld.off * ldb + ld.n0;
+    al.template load<SET>(lk, [&](int k) { return Ap + (size_t)k * lda; });
+    bl.template load<SET>(lk, [&](int k) { return Bp + (size_t)k * ldb; });
+    if (lk + 1 < ld.nk) ++lk;
+    else if (li + K < list.count) { li += K; ld = list.item(li); lk = 0; }
+  };
   f32x16 acc[C::FM][C::FN];
-  auto aload = [&](auto& l, int kt, auto set) {
-    l.template load<decltype(set)::value>(kt, [&](int k) {
-      return GATE_UP ? Ap + (size_t)(off + k) * 2 * I + m0 : Ap + (size_t)(off + k) * H + m0;
-    });
-  };
-  auto bload = [&](auto& l, int kt, auto set) {
-    l.template load<decltype(set)::value>(kt, [&](int k) {
-      return GATE_UP ? Bp + (size_t)(off + k) * H + n0 : Bp + (size_t)(off + k) * I + n0;
-    });
-  };
-  if constexpr (kNLayout<C>) mainloop_pf1<C, true, true>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
-  else mainloop_pf1<C>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
-  OutT* dW = (OutT*)g.out0 + (size_t)e * M * N;
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
-    if (m >= M) continue;
+  for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
-        if (n < N)
-          store4<OutT>(dW + (size_t)m * N + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1],
-                       acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  // After the step's barrier: stage a finished tile, then a second barrier.
+  auto finish_step = [&](int st) {
+    if (st < total && ck + 1 == cur.nk) {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const int r = wm * C::WTM + fm * 32 + (lane & 31);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int vg = 0; vg < 4; ++vg) {
+            const int c4 = (wn * C::WTN + fn * 32 + acc_col4(vg, lane)) >> 2;
+            *(float4*)(stage + stage_off<C>(r, c4)) =
+                make_float4(acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
+                            acc[fm][fn][vg * 4 + 3]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[fm][fn][vg * 4 + v] = 0.f;
+          }
       }
+      __syncthreads();   // tile staged
+    }
+  };
+  T* As0 = lds;
+  T* As1 = lds + C::A_ELEMS;
+  T* Bs0 = lds + 2 * C::A_ELEMS;
+  T* Bs1 = Bs0 + C::B_ELEMS;
+  issue(Set<0>{});
+  issue(Set<1>{});
+  al.template store<0>(As0);
+  bl.template store<0>(Bs0);
+  __syncthreads();   // prologue
+  // The step count is padded to even, so the loop has no exit between its
+  // two halves and every half stores its register set to LDS (a branch
+  // around those stores, or an exit between them, makes the compiler wait for
+  // all loads at the loop head).  A padding step multiplies into accumulators
+  // that are never staged.
+  for (int st = 0; st < total_even; st += 2) {
+    // even step: LDS buffer 0 holds this step, register set 1 the next one
+    issue(Set<0>{});
+    mma_tile<C, kNLayout<C>, kNLayout<C>>(As0, Bs0, acc);
+    al.template store<1>(As1);
+    bl.template store<1>(Bs1);
+    __syncthreads();   // step done
+    finish_step(st);
+    next_step();
+    // odd step: LDS buffer 1 holds this step, register set 0 the next one
+    issue(Set<1>{});
+    mma_tile<C, kNLayout<C>, kNLayout<C>>(As1, Bs1, acc);
+    al.template store<0>(As0);
+    bl.template store<0>(Bs0);
+    __syncthreads();   // step done
+    finish_step(st + 1);
+    next_step();
   }
 }
 
 // ------------------------------------------------------------------ host side
 using CfgB = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // bf16
 using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
-// weight gradients: half the LDS per workgroup, so three share a CU
-using CfgWB = Cfg<uint16_t, 128, 128, 32, 2, 2>;
+// weight gradients (one persistent workgroup per CU: operands, staging tile and tables in LDS)
+using CfgWB = Cfg<uint16_t, 128, 128, 64, 2, 4>;
 using CfgWF = Cfg<float, 128, 128, 16, 2, 2>;
 
 static constexpr int log2_bm_index(int bm) { return bm == 32 ? 0 : bm == 64 ? 1 : bm == 128 ? 2 : 3; }
@@ -921,17 +1171,30 @@ hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const voi
                        : gate_up_dgrad_impl<CfgF>(pb, dZ, Wgu, dXp, s);
 }
 
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    return 8;
+  return cus;
+}
+
 template <class C, bool GU, typename OutT>
 static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
+  const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
+  if (pb.S == 0) return launch_fill_zero(dW, (size_t)pb.E * M * N * sizeof(OutT), s);   // no positions
   GArgs g = base_args(pb, C::BM);
   g.A = A; g.B = B; g.out0 = dW;
-  const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
   g.ntm = (M + C::BM - 1) / C::BM;
   g.ntn = (N + C::BN - 1) / C::BN;
-  const long total = (long)pb.E * g.ntm * g.ntn;
-  const long grid = ((total + 63) / 64) * 64;   // whole chunks of 8 tiles on each of the 8 XCDs
+  // split experts: more than twice the mean positions per expert (and more than 4 k-steps)
+  const long mean = ((long)pb.S + pb.E - 1) / pb.E;
+  g.big = (int)std::max<long>(2 * mean, 4 * C::BK);
+  // one persistent workgroup per CU, a whole number per XCD
+  static const int cus = device_cus();
+  const long grid = (cus / 8) * 8;
   return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s,
-                    [&] { wgrad_kernel<C, GU, OutT><<<grid, C::NT, 0, s>>>(g); });
+                    [&] { wgrad_kernel<C, GU, OutT><<<grid, C::NT + kStoreThreads, 0, s>>>(g); });
 }
 
 template <bool GU>

@@ -71,8 +71,8 @@ def test_argument_errors_before_launch():
     d.dtype = 7
     assert _call_fwd(d) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_fwd(None, p, p, p, p, p, p, None, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
-    # T = 0 is a valid no-op for the forward
-    assert _call_fwd(moe.make_desc(0, 128, 128, 8, 2)) == _lib.MOE_OK
+    # (T = 0 passes these checks and then clears the status word on the device:
+    # covered by the GPU tests)
 
 
 def test_bwd_argument_errors():

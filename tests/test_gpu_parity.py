@@ -149,3 +149,32 @@ def test_clamps_exercised():
                   for s in range(T * K)])
     assert np.mean(np.abs(z) > 7) > 0.05
     run_and_compare(inp, grad_dtype="fp32")
+
+
+@pytest.mark.parametrize("grad_dtype", ["fp32", "bf16"])
+def test_no_tokens_gives_zero_weight_grads(grad_dtype):
+    """T = 0: every expert is empty, so every weight gradient is exactly zero
+    (the outputs start as NaN, so a tile the kernels skip would show)."""
+    H, I, E, K = 264, 136, 5, 2
+    dev = "cuda"
+    g = torch.Generator(device="cpu").manual_seed(7)
+    wgu = torch.randn(E, 2 * I, H, generator=g).to(torch.bfloat16).to(dev)
+    wd = torch.randn(E, H, I, generator=g).to(torch.bfloat16).to(dev)
+    hidden = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((0, K), dtype=torch.int32, device=dev)
+    w = torch.empty((0, K), dtype=torch.float32, device=dev)
+    d_out = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    gdt = torch.float32 if grad_dtype == "fp32" else torch.bfloat16
+    grads = (torch.empty((0, H), dtype=torch.bfloat16, device=dev), torch.empty((0, K), dtype=torch.float32, device=dev),
+             torch.full((E, 2 * I, H), float("nan"), dtype=gdt, device=dev),
+             torch.full((E, H, I), float("nan"), dtype=gdt, device=dev))
+    # a workspace whose status word holds a stale flag: the T = 0 calls clear it
+    _, bws, _ = moe.workspace_size(moe.make_desc(0, H, I, E, K, grad_dtype=grad_dtype))
+    ws = torch.full((bws,), 7, dtype=torch.uint8, device=dev)
+    out, _, ws = moe.fwd(hidden, ids, w, wgu, wd, ws=ws)
+    assert moe.check_device_status(ws) == 0 and out.shape == (0, H)
+    ws.fill_(7)
+    _, _, dgu, dd, ws = moe.bwd(hidden, ids, w, wgu, wd, d_out, grads=grads, grad_dtype=grad_dtype, ws=ws)
+    torch.cuda.synchronize()
+    assert moe.check_device_status(ws) == 0
+    assert bool((dgu == 0).all()) and bool((dd == 0).all())
