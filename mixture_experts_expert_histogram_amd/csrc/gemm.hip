@@ -103,14 +103,19 @@ struct Cfg {
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int VEC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
   static constexpr int CPR = BK / VEC;                 // chunks per LDS row
-  static constexpr int SW = CPR < 8 ? CPR : 8;         // swizzle period
+  // LDS is read 16 lanes at a time, 16 bytes each: one 256-byte bank window.
+  // A fragment read takes one 16-byte chunk from each of 16 consecutive rows,
+  // so the chunk index is XORed with the row's window index (rows per window
+  // = 16 / CPR) and 16 consecutive rows land in 16 distinct slots.
+  static constexpr int SW = CPR < 16 ? CPR : 16;       // swizzle period
+  static constexpr int RPW = CPR < 16 ? 16 / CPR : 1;  // rows per 256-byte window
   static constexpr int KSTEP = sizeof(T) == 2 ? 16 : 2;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * (int)sizeof(T);
   static_assert((CPR & (CPR - 1)) == 0, "chunks per row must be a power of two");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   __device__ static __forceinline__ int lds_off(int row, int chunk) {
-    return row * BK + ((chunk ^ (row & (SW - 1))) * VEC);
+    return row * BK + ((chunk ^ ((row / RPW) & (SW - 1))) * VEC);
   }
 };
 
