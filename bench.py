@@ -32,7 +32,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="gptoss", help="synthetic workload name (synth.WORKLOADS)")
-    p.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"])
+    p.add_argument("--grad-dtype", default="bf16", choices=["fp32", "bf16"],
+                   help="weight-gradient storage (accumulation is fp32 either way); bf16 is the parameter dtype")
+    p.add_argument("--no-alt-grad-dtype", action="store_true",
+                   help="skip the extra timing of the same steps with fp32 weight-gradient storage")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle's CPU sample")
     p.add_argument("--no-kernel-timing", action="store_true")
@@ -66,16 +69,18 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, grad_dtype):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None if there is none or the kernel sources changed since it was taken."""
+    None if there is none, it was taken on another workload or weight-gradient
+    dtype, or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+    if (rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload
+            or rec.get("grad_dtype") != grad_dtype):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
@@ -254,7 +259,33 @@ def main():
         kern_avg = {k: round(ms / n, 4) for k, (n, ms) in kernels.items()}
         dominant = max((k for k in kernels if k in model), key=lambda k: kernels[k][1])
         roof = roofline_for(dominant, kernels[dominant][1] / kernels[dominant][0], model)
-        roof["traffic"] = measured_traffic(dominant, wl.name)
+        roof["traffic"] = measured_traffic(dominant, wl.name, args.grad_dtype)
+
+    # The same steps with fp32 weight-gradient storage (context for the dtype reading).
+    alt = None
+    if args.grad_dtype == "bf16" and not args.no_alt_grad_dtype:
+        d32 = moe.make_desc(wl.T, wl.H, wl.I, wl.E, wl.K, wl.dtype, wl.act, wl.layout, wl.limit, wl.alpha, "fp32")
+        ws_b32 = moe.empty_workspace(moe.workspace_size(d32)[1], dev)
+        grads32 = (grads[0], grads[1], torch.empty(Wgu.shape, dtype=torch.float32, device=dev),
+                   torch.empty(Wd.shape, dtype=torch.float32, device=dev))
+
+        def step32():
+            fwd()
+            moe.bwd(X, ids, w, Wgu, Wd, dY, saved=saved, ws=ws_b32, grads=grads32, grad_dtype="fp32", **kw)
+
+        for _ in range(args.warmup):
+            step32()
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.steps):
+            step32()
+        t_stop.record()
+        torch.cuda.synchronize()
+        ms32 = t_start.elapsed_time(t_stop) / args.steps
+        alt = {"grad_dtype": "fp32", "ms_per_step": round(ms32, 4),
+               "value": round((flops_fwd + flops_bwd) / (ms32 * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
+        del grads32, ws_b32
+        print(f"[bench] fp32 weight grads: {ms32:.3f} ms/step", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -276,7 +307,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: routed MoE layer forward+backward, T={wl.T} H={wl.H} I={wl.I} "
                                f"E={wl.E} top-{wl.K}, {wl.act} GLU, gate/up {wl.layout}, "
-                               f"{wl.routing} routing, {args.grad_dtype} weight grads, saved Z",
+                               f"{wl.routing} routing, {args.grad_dtype} weight grads "
+                               f"(fp32 accumulation), saved Z",
                    "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K, "parallelism": "single GPU"},
         "fwd_ms": round(fm, 4),
         "bwd_ms": round(bm, 4),
@@ -285,6 +317,7 @@ def main():
         "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
         "kernels_avg_ms": kern_avg,
+        "fp32_weight_grads": alt,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -1,5 +1,7 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times (moe_fwd with saved Z, then moe_bwd; fp32 weight gradients).
+benchmark times (moe_fwd with saved Z, then moe_bwd; weight gradients
+accumulated in fp32 and stored as bf16, the parameter dtype; fp32 storage is
+checked on the gpt-oss workload too).
 
 The fp64 oracle cannot evaluate a whole layer at these sizes in test time, so
 it checks samples it can compute one by one:
@@ -28,9 +30,10 @@ pytestmark = pytest.mark.gpu
 _cache = {}
 
 
-def run_workload(name):
-    if name in _cache:
-        return _cache[name]
+def run_workload(name, grad_dtype="bf16"):
+    key = (name, grad_dtype)
+    if key in _cache:
+        return _cache[key]
     _cache.clear()
     torch.cuda.empty_cache()
     wl = WORKLOADS[name]
@@ -43,12 +46,12 @@ def run_workload(name):
     kw = dict(act=wl.act, layout=wl.layout, limit=wl.limit, alpha=wl.alpha)
     out, saved, ws = moe.fwd(d["hidden"], d["topk_ids"], d["topk_weights"], Wgu, Wd, save=True, **kw)
     dh, dw, dgu, dd, ws2 = moe.bwd(d["hidden"], d["topk_ids"], d["topk_weights"], Wgu, Wd, d["d_out"],
-                                   saved=saved, grad_dtype="fp32", **kw)
+                                   saved=saved, grad_dtype=grad_dtype, **kw)
     torch.cuda.synchronize()
     assert moe.check_device_status(ws) == 0 and moe.check_device_status(ws2) == 0
     del saved, ws, ws2
     res = dict(wl=wl, ids=ids, w=w, X=X, dY=dY, Wgu=Wgu, Wd=Wd, out=out, dh=dh, dw=dw, dgu=dgu, dd=dd)
-    _cache[name] = res
+    _cache[key] = res
     return res
 
 
@@ -101,7 +104,16 @@ def halves(x, layout):
 @pytest.mark.parametrize("name,which", [("gptoss", "coldest"), ("gptoss", "median"), ("backward", "coldest"),
                                         ("backward", "median"), ("zipf", "coldest"), ("zipf", "median")])
 def test_backward_sampled_experts(name, which):
-    r = run_workload(name)
+    check_sampled_expert(run_workload(name), which)
+
+
+@pytest.mark.parametrize("which", ["coldest", "median"])
+def test_fp32_weight_grads_sampled_experts(which):
+    check_sampled_expert(run_workload("gptoss", "fp32"), which)
+
+
+def check_sampled_expert(r, which):
+    name = r["wl"].name
     wl = r["wl"]
     counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
     nonempty = [e for e in np.argsort(counts, kind="stable") if counts[e] > 0]
