@@ -546,11 +546,12 @@ template <class C, int ROT>
 using MNLoader = std::conditional_t<sizeof(typename C::elem) == 2, NLoader<C, ROT>, TransLoader<C, 128, ROT>>;
 template <class C> constexpr bool kNLayout = sizeof(typename C::elem) == 2;
 
-// bf16 operands fit two register sets in 256 VGPRs; fp32 ones use one.
+// bf16 operands fit two register sets in 256 VGPRs up to 128-row tiles;
+// 192-row tiles and fp32 operands use one.
 template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop_rows(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                               typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
-  if constexpr (sizeof(typename C::elem) == 2) mainloop<C>(al, bl, aload, bload, nk, lds, acc);
+  if constexpr (sizeof(typename C::elem) == 2 && C::BM <= 128) mainloop<C>(al, bl, aload, bload, nk, lds, acc);
   else mainloop_pf1<C>(al, bl, aload, bload, nk, lds, acc);
 }
 
@@ -678,8 +679,8 @@ __global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
   auto bload = [&](auto& l, int kt, auto set) {
     l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * I + n0; });
   };
-  if constexpr (kNLayout<C>) mainloop<C, false, true>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
-  else mainloop_pf1<C>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
+  if constexpr (kNLayout<C> && C::BM <= 128) mainloop<C, false, true>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
+  else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
 
   const float* Z = (const float*)g.Z;
   T* dZ = (T*)g.out0;
@@ -759,8 +760,8 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
   auto bload = [&](auto& l, int kt, auto set) {
     l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * H + n0; });
   };
-  if constexpr (kNLayout<C>) mainloop<C, false, true>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
-  else mainloop_pf1<C>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
+  if constexpr (kNLayout<C> && C::BM <= 128) mainloop<C, false, true>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
+  else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
   float* dXp = (float*)g.out0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
@@ -1073,18 +1074,26 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 
 // ------------------------------------------------------------------ host side
 using CfgB = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // bf16
+// bf16 with 192-row M-tiles (96 rows per wave): when experts average a little
+// over 128 positions, 128-row tiles leave a mostly empty second tile per
+// expert that repeats the whole weight stream; one 192-row tile covers them.
+using CfgB192 = Cfg<uint16_t, 192, 128, 64, 2, 2>;
+static bool use_bm192(const GemmProblem& pb) {
+  const long mean = pb.E > 0 ? (long)pb.S / pb.E : 0;
+  return pb.dtype == 0 && mean > 100 && mean <= 176;
+}
 using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
 // weight gradients (one persistent workgroup per CU: operands, staging tile and tables in LDS)
 using CfgWB = Cfg<uint16_t, 128, 128, 64, 2, 4>;
 using CfgWF = Cfg<float, 128, 128, 16, 2, 2>;
 
-static constexpr int log2_bm_index(int bm) { return bm == 32 ? 0 : bm == 64 ? 1 : bm == 128 ? 2 : 3; }
+static constexpr int bm_index(int bm) { return bm == 32 ? 0 : bm == 64 ? 1 : bm == 128 ? 2 : bm == 256 ? 3 : 4; }
 
 static GArgs base_args(const GemmProblem& pb, int bm) {
   GArgs g = {};
   const RouteState& rs = *pb.rs;
   g.offsets = rs.offsets;
-  g.tile_prefix = rs.tile_prefix + log2_bm_index(bm) * (pb.E + 1);
+  g.tile_prefix = rs.tile_prefix + bm_index(bm) * (pb.E + 1);
   g.tok_of_pos = rs.tok_of_pos;
   g.w_of_pos = rs.w_of_pos;
   g.expert_order = rs.expert_order;
@@ -1121,8 +1130,9 @@ static hipError_t gate_up_dispatch(const GemmProblem& pb, const void* X, const v
 hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
                           hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
-  return pb.dtype == 0 ? gate_up_dispatch<CfgB>(pb, X, Wgu, a_out, z_out, s)
-                       : gate_up_dispatch<CfgF>(pb, X, Wgu, a_out, z_out, s);
+  if (pb.dtype != 0) return gate_up_dispatch<CfgF>(pb, X, Wgu, a_out, z_out, s);
+  return use_bm192(pb) ? gate_up_dispatch<CfgB192>(pb, X, Wgu, a_out, z_out, s)
+                       : gate_up_dispatch<CfgB>(pb, X, Wgu, a_out, z_out, s);
 }
 
 template <class C>
@@ -1136,7 +1146,8 @@ static hipError_t down_impl(const GemmProblem& pb, const void* a, const void* Wd
 
 hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
-  return pb.dtype == 0 ? down_impl<CfgB>(pb, a, Wd, Yp, s) : down_impl<CfgF>(pb, a, Wd, Yp, s);
+  if (pb.dtype != 0) return down_impl<CfgF>(pb, a, Wd, Yp, s);
+  return use_bm192(pb) ? down_impl<CfgB192>(pb, a, Wd, Yp, s) : down_impl<CfgB>(pb, a, Wd, Yp, s);
 }
 
 int down_dgrad_nparts(int I) { return (I + 127) / 128; }   // both configs use BN = 128
@@ -1156,6 +1167,8 @@ hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* 
                              void* aw, float* partials, int* nparts, hipStream_t s) {
   *nparts = down_dgrad_nparts(pb.I);
   if (pb.S == 0) return hipSuccess;
+  // (192-row tiles measured no faster here: its GLU-backward epilogue leaves
+  // room for only one register set of prefetch at that height)
   return pb.dtype == 0 ? down_dgrad_impl<CfgB>(pb, dY, Wd, Z, dZ, aw, partials, s)
                        : down_dgrad_impl<CfgF>(pb, dY, Wd, Z, dZ, aw, partials, s);
 }
@@ -1172,8 +1185,9 @@ static hipError_t gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, cons
 
 hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
-  return pb.dtype == 0 ? gate_up_dgrad_impl<CfgB>(pb, dZ, Wgu, dXp, s)
-                       : gate_up_dgrad_impl<CfgF>(pb, dZ, Wgu, dXp, s);
+  if (pb.dtype != 0) return gate_up_dgrad_impl<CfgF>(pb, dZ, Wgu, dXp, s);
+  return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(pb, dZ, Wgu, dXp, s)
+                       : gate_up_dgrad_impl<CfgB>(pb, dZ, Wgu, dXp, s);
 }
 
 static int device_cus() {

@@ -11,8 +11,8 @@ constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_CHUNK = 2048;
 constexpr int MAX_E = 1024;
 // M-tile heights for which the routing scan writes a tile prefix table.
-constexpr int N_TILE_BM = 4;              // 32, 64, 128, 256
-__host__ __device__ constexpr int tile_bm(int j) { return 32 << j; }
+constexpr int N_TILE_BM = 5;              // 32, 64, 128, 256, 192
+__host__ __device__ constexpr int tile_bm(int j) { return j < 4 ? 32 << j : 192; }
 
 // Device views of the routing state that lives in the workspace.
 struct RouteState {
