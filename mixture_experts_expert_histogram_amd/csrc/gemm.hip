@@ -882,11 +882,32 @@ struct WgradList {
   }
 };
 
-// Staging tile: [BM rows][BN fp32], 16-byte chunks XOR-swizzled by row.
-template <class C>
-__device__ __forceinline__ int stage_off(int r, int c4) {
-  return r * C::BN + ((c4 ^ (r & 31)) << 2);
-}
+// Staging tile: [BM rows][BN values of the output type], 16-byte chunks
+// XOR-swizzled by row, so the MMA lanes' writes (32 consecutive rows, one
+// column group) and the store waves' reads (one row's chunks) spread over the
+// banks.  bf16: a lane writes 8 bytes (4 values), half a chunk; the half is
+// flipped for rows 16-31 of each 32-row group, so rows r and r+16 (same
+// swizzled chunk) use different halves.
+template <class C, typename OutT>
+struct Stage {
+  static constexpr int ROW = C::BN * (int)sizeof(OutT);   // bytes per row
+  static constexpr int CPR = ROW / 16;                     // 16-byte chunks per row
+  static constexpr int BYTES = C::BM * ROW;
+  static_assert(CPR == 16 || CPR == 32, "staging rows of 256 or 512 bytes");
+  __device__ static __forceinline__ int chunk(int r, int ch) { return r * ROW + ((ch ^ (r & (CPR - 1))) << 4); }
+  // byte offset of output columns 4*c4 .. 4*c4+3 of row r
+  __device__ static __forceinline__ int quad(int r, int c4) {
+    if constexpr (sizeof(OutT) == 4) return chunk(r, c4);
+    else return chunk(r, c4 >> 1) + ((((c4 & 1) ^ ((r >> 4) & 1))) << 3);
+  }
+  // 16-byte chunk ch of row r as stored (bf16 halves in column order)
+  __device__ static __forceinline__ uint4 read(const char* stage, int r, int ch) {
+    uint4 v = *(const uint4*)(stage + chunk(r, ch));
+    if constexpr (sizeof(OutT) == 2)
+      if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+    return v;
+  }
+};
 
 constexpr int kStoreThreads = 256;   // four store waves
 
@@ -894,9 +915,10 @@ template <class C, bool GATE_UP, typename OutT>
 __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g) {
   using T = typename C::elem;
   static_assert(C::BN == 128, "store waves copy 32 chunks per row");
-  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES + C::BM * C::BN * 4];
+  using ST = Stage<C, OutT>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES + ST::BYTES];
   T* lds = (T*)smem_raw;
-  float* stage = (float*)(smem_raw + C::LDS_BYTES);
+  char* stage = smem_raw + C::LDS_BYTES;
   const int H = g.H, I = g.I;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
   const int lda = M, ldb = N;       // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
@@ -940,10 +962,11 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
     // all of it at once would block the store waves on a saturated write
     // path and hold up the MMA waves at the next barrier.
     const int tid = threadIdx.x - C::NT;
-    constexpr int PER = C::BM * 32 / kStoreThreads;
+    constexpr int PER = C::BM * ST::CPR / kStoreThreads;   // 16-byte chunks per thread
     constexpr int NQ = 4, QS = PER / NQ;
+    constexpr int VPC = 16 / (int)sizeof(OutT);             // values per chunk
     static_assert(PER % NQ == 0, "store quarters");
-    float4 v[PER];
+    uint4 v[PER];
     OutT* dWt = dW;        // tile origin in dW of the registers' tile
     int next_q = NQ;       // next quarter to write (NQ: none pending)
     int stage_rows = 0, stage_cols = 0;
@@ -955,9 +978,8 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
         for (int j = 0; j < QS; ++j) {
           const int i = qq * QS + j;
           const int idx = tid + i * kStoreThreads;
-          const int r = idx >> 5, c = (idx & 31) * 4;
-          if (r < stage_rows && c < stage_cols)
-            store4<OutT>(dWt + (size_t)r * N + c, v[i].x, v[i].y, v[i].z, v[i].w);
+          const int r = idx / ST::CPR, c = (idx % ST::CPR) * VPC;
+          if (r < stage_rows && c < stage_cols) *(uint4*)(dWt + (size_t)r * N + c) = v[i];
         }
       }
     };
@@ -971,7 +993,7 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
           const int idx = tid + i * kStoreThreads;
-          v[i] = *(const float4*)(stage + stage_off<C>(idx >> 5, idx & 31));
+          v[i] = ST::read(stage, idx / ST::CPR, idx % ST::CPR);
         }
         dWt = dW + ((size_t)cur.e * M + cur.m0) * N + cur.n0;
         stage_rows = min(C::BM, M - cur.m0);
@@ -1028,9 +1050,8 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 #pragma unroll
           for (int vg = 0; vg < 4; ++vg) {
             const int c4 = (wn * C::WTN + fn * 32 + acc_col4(vg, lane)) >> 2;
-            *(float4*)(stage + stage_off<C>(r, c4)) =
-                make_float4(acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
-                            acc[fm][fn][vg * 4 + 3]);
+            store4<OutT>((OutT*)(stage + ST::quad(r, c4)), acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1],
+                         acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[fm][fn][vg * 4 + v] = 0.f;
           }
