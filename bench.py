@@ -41,6 +41,14 @@ def parse():
     p.add_argument("--no-kernel-timing", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    p.add_argument("--protocol", action="store_true",
+                   help="time every workload's passes (forward with Z saved or not, backward with saved Z or "
+                        "recomputing it) with a cache flush between iterations; one JSON line per case")
+    p.add_argument("--sweep", action="store_true",
+                   help="token-count sweep: 16 values of T per layer shape, forward and backward; "
+                        "one JSON line per case and a mean-latency line per shape")
+    p.add_argument("--shapes", default="gptoss,large,backward", help="layer shapes of --sweep")
+    p.add_argument("--iters", type=int, default=20, help="timed iterations per case of --protocol / --sweep")
     return p.parse_args()
 
 
@@ -126,6 +134,182 @@ def roofline_for(name, avg_ms, model):
             "algorithmic_bytes": nbytes, "flops": flops}
 
 
+# ------------------------------------------------------------------ per-pass roofline
+def pass_model(wl, counts, pass_, grad_bytes):
+    """Useful flops, algorithmic HBM bytes and weight-stream bytes of one pass.
+
+    Useful flops count the routed work only: 6*S*H*I forward, 12*S*H*I
+    backward (a Z recompute is not useful work).  Algorithmic bytes are the
+    weights of the experts that receive slots (read), the hidden states in
+    and the output out (forward); the backward adds the output gradient in,
+    the input gradient out and every expert's weight gradient out (the
+    outputs are fully written, zeros for experts without slots).
+    Intermediates (the activation, Z, the permuted rows) are not counted.
+    """
+    S, T, H, I, E = wl.S, wl.T, wl.H, wl.I, wl.E
+    eb = 2 if wl.dtype == "bf16" else 4
+    touched = int((counts > 0).sum())
+    w_read = touched * 3 * H * I * eb
+    route = T * wl.K * 8
+    if pass_ == "fwd":
+        flops = 6.0 * S * H * I
+        nbytes = w_read + 2 * T * H * eb + route
+        stream = w_read
+    else:
+        flops = 12.0 * S * H * I
+        dw = E * 3 * H * I * grad_bytes
+        nbytes = w_read + dw + 3 * T * H * eb + route + T * wl.K * 4
+        stream = w_read + dw
+    return flops, nbytes, stream
+
+
+def pass_record(wl, counts, pass_, grad_bytes, times_ms):
+    import numpy as np
+    flops, nbytes, stream = pass_model(wl, counts, pass_, grad_bytes)
+    t = np.asarray(times_ms, dtype=np.float64)
+    med, mn, mean = float(np.median(t)), float(t.min()), float(t.mean())
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+    t_roof = max(t_mfma, t_hbm)
+    return {"median_ms": round(med, 4), "min_ms": round(mn, 4), "mean_ms": round(mean, 4),
+            "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+            "pct_of_bf16_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "bound": "mfma" if t_mfma >= t_hbm else "hbm", "t_roof_ms": round(t_roof, 4),
+            "pct_of_roofline": round(100 * t_roof / med, 2),
+            "weight_stream_gbps": round(stream / (med * 1e-3) / 1e9, 1),
+            "useful_gflop": round(flops / 1e9, 1), "algorithmic_gb": round(nbytes / 1e9, 3),
+            "experts_with_slots": int((counts > 0).sum())}
+
+
+class PassRunner:
+    """Resident inputs, weights, outputs and workspaces of one workload, and
+    the timing of its passes with a 512 MiB write between iterations (larger
+    than the 256 MiB last-level cache, so activations start cold as the
+    weights do)."""
+
+    FLUSH_BYTES = 512 << 20
+
+    def __init__(self, wl, dev, weights=None, grad_dtype="bf16", seed=0):
+        import numpy as np
+        import torch
+        import mixture_experts_expert_histogram_amd as moe
+        from synth import device_weights, make_dout, make_hidden, make_routing, to_device
+        self.moe, self.torch, self.wl, self.grad_dtype = moe, torch, wl, grad_dtype
+        ids_np, w_np = make_routing(wl, seed=seed)
+        self.counts = np.bincount(ids_np.ravel(), minlength=wl.E)
+        self.X = to_device(make_hidden(wl, seed), wl, dev)
+        self.dY = to_device(make_dout(wl, seed), wl, dev)
+        self.ids = torch.from_numpy(ids_np).to(dev)
+        self.w = torch.from_numpy(w_np).to(dev)
+        self.Wgu, self.Wd = weights if weights is not None else device_weights(wl, dev, seed=seed)
+        self.kw = dict(act=wl.act, layout=wl.layout, limit=wl.limit, alpha=wl.alpha)
+        desc = moe.make_desc(wl.T, wl.H, wl.I, wl.E, wl.K, wl.dtype, wl.act, wl.layout, wl.limit, wl.alpha,
+                             grad_dtype)
+        fws, bws, sbytes = moe.workspace_size(desc)
+        self.ws_f, self.ws_b = moe.empty_workspace(fws, dev), moe.empty_workspace(bws, dev)
+        self.saved = moe.empty_workspace(sbytes, dev)
+        self.out = torch.empty_like(self.X)
+        gdt = torch.float32 if grad_dtype == "fp32" else torch.bfloat16
+        self.grads = (torch.empty_like(self.X), torch.empty((wl.T, wl.K), dtype=torch.float32, device=dev),
+                      torch.empty(self.Wgu.shape, dtype=gdt, device=dev),
+                      torch.empty(self.Wd.shape, dtype=gdt, device=dev))
+        self.flush = torch.empty(self.FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.grad_bytes = 4 if grad_dtype == "fp32" else 2
+
+    def fwd(self, save):
+        self.moe.fwd(self.X, self.ids, self.w, self.Wgu, self.Wd, save=save, ws=self.ws_f, out=self.out,
+                     saved=self.saved if save else None, **self.kw)
+
+    def bwd(self, saved):
+        self.moe.bwd(self.X, self.ids, self.w, self.Wgu, self.Wd, self.dY, saved=self.saved if saved else None,
+                     ws=self.ws_b, grads=self.grads, grad_dtype=self.grad_dtype, **self.kw)
+
+    def time(self, fn, warmup, iters):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            self.flush.fill_(1)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        if self.moe.check_device_status(self.ws_f) != 0:
+            raise RuntimeError("bad expert id reported by the device")
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def run_pass(self, pass_, saved, warmup, iters):
+        if pass_ == "fwd":
+            times = self.time(lambda: self.fwd(saved), warmup, iters)
+        else:
+            self.fwd(True)          # untimed: routing and Z for the backward
+            times = self.time(lambda: self.bwd(saved), warmup, iters)
+        return pass_record(self.wl, self.counts, pass_, self.grad_bytes, times)
+
+
+# The passes timed per workload: the gpt-oss and large shapes' forward without
+# Z kept; the backward workload's backward with saved Z and recomputing it;
+# the Zipf workload's forward with and without Z kept and its backward both ways.
+PROTOCOL = [("gptoss", "fwd", False), ("gptoss", "fwd", True), ("gptoss", "bwd", True), ("gptoss", "bwd", False),
+            ("large", "fwd", False),
+            ("backward", "bwd", True), ("backward", "bwd", False),
+            ("zipf", "fwd", True), ("zipf", "fwd", False), ("zipf", "bwd", True), ("zipf", "bwd", False)]
+
+
+def run_protocol(args):
+    import torch
+    from synth import WORKLOADS
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    current, runner = None, None
+    for name, pass_, saved in PROTOCOL:
+        if name != current:
+            runner = None
+            torch.cuda.empty_cache()
+            print(f"[protocol] {name}: drawing inputs", file=sys.stderr, flush=True)
+            runner = PassRunner(WORKLOADS[name], dev, grad_dtype=args.grad_dtype)
+            current = name
+        rec = runner.run_pass(pass_, saved, args.warmup, args.iters)
+        wl = runner.wl
+        mode = ("Z saved" if saved else "Z not kept") if pass_ == "fwd" else ("saved Z" if saved else "recompute Z")
+        line = {"workload": name, "pass": pass_, "mode": mode, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
+                "K": wl.K, "grad_dtype": args.grad_dtype if pass_ == "bwd" else None,
+                "iters": args.iters, "warmup": args.warmup}
+        line.update(rec)
+        print(json.dumps(line), flush=True)
+
+
+SWEEP_T = [1 << k for k in range(16)]     # 16 token counts per shape, 1 .. 32768
+
+
+def run_sweep(args):
+    import numpy as np
+    import torch
+    from synth import WORKLOADS, device_weights
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for name in args.shapes.split(","):
+        base = WORKLOADS[name]
+        torch.cuda.empty_cache()
+        weights = device_weights(base, dev, seed=0)
+        lat = {"fwd": [], "bwd": []}
+        for T in SWEEP_T:
+            wl = base.with_(T=T)
+            runner = PassRunner(wl, dev, weights=weights, grad_dtype=args.grad_dtype)
+            for pass_ in ("fwd", "bwd"):
+                rec = runner.run_pass(pass_, pass_ == "bwd", args.warmup, args.iters)
+                lat[pass_].append(rec["mean_ms"])
+                line = {"shape": name, "pass": pass_, "T": T, "S": wl.S}
+                line.update(rec)
+                print(json.dumps(line), flush=True)
+            del runner
+        for pass_ in ("fwd", "bwd"):
+            print(json.dumps({"shape": name, "pass": pass_, "cases": len(SWEEP_T),
+                              "mean_latency_ms": round(float(np.mean(lat[pass_])), 4)}), flush=True)
+        del weights
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(wl, ids, w, X, dY, Wgu_dev, Wd_dev, budget_s):
     """The fp64 oracle on a bounded sample: whole experts of this workload,
@@ -175,6 +359,12 @@ def main():
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); "
               "the expert-parallel multi-GPU path is not part of this library", file=sys.stderr)
         sys.exit(2)
+    if args.protocol:
+        run_protocol(args)
+        return
+    if args.sweep:
+        run_sweep(args)
+        return
     import numpy as np
     import torch
 

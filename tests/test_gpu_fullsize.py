@@ -23,26 +23,38 @@ import torch
 import mixture_experts_expert_histogram_amd as moe
 import oracle
 from synth import WORKLOADS, device_weights, make_dout, make_hidden, make_routing, to_device
-from tests._gpu import assert_parity, host
+from tests._gpu import assert_parity, assert_parity_slots, host, slot_factors
 
 pytestmark = pytest.mark.gpu
 
 _cache = {}
+_weights = {}
 
 
-def run_workload(name, grad_dtype="bf16"):
-    key = (name, grad_dtype)
+def shape_weights(name):
+    """Device expert weights of a workload's layer shape, kept while tests of
+    that shape run (at several token counts)."""
+    if name not in _weights:
+        _weights.clear()
+        _cache.clear()
+        torch.cuda.empty_cache()
+        _weights[name] = device_weights(WORKLOADS[name], "cuda", seed=0)
+    return _weights[name]
+
+
+def run_workload(name, grad_dtype="bf16", T=None):
+    key = (name, grad_dtype, T)
     if key in _cache:
         return _cache[key]
     _cache.clear()
     torch.cuda.empty_cache()
-    wl = WORKLOADS[name]
+    wl = WORKLOADS[name] if T is None else WORKLOADS[name].with_(T=T)
     dev = "cuda"
     ids, w = make_routing(wl, seed=0)
     X, dY = make_hidden(wl, 0), make_dout(wl, 0)
     d = dict(hidden=to_device(X, wl, dev), topk_ids=torch.from_numpy(ids).to(dev),
              topk_weights=torch.from_numpy(w).to(dev), d_out=to_device(dY, wl, dev))
-    Wgu, Wd = device_weights(wl, dev, seed=0)
+    Wgu, Wd = shape_weights(name)
     kw = dict(act=wl.act, layout=wl.layout, limit=wl.limit, alpha=wl.alpha)
     out, saved, ws = moe.fwd(d["hidden"], d["topk_ids"], d["topk_weights"], Wgu, Wd, save=True, **kw)
     dh, dw, dgu, dd, ws2 = moe.bwd(d["hidden"], d["topk_ids"], d["topk_weights"], Wgu, Wd, d["d_out"],
@@ -117,7 +129,7 @@ def check_sampled_expert(r, which):
     wl = r["wl"]
     counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
     nonempty = [e for e in np.argsort(counts, kind="stable") if counts[e] > 0]
-    e = nonempty[0] if which == "coldest" else nonempty[len(nonempty) // 2]
+    e = {"coldest": nonempty[0], "median": nonempty[len(nonempty) // 2], "hottest": nonempty[-1]}[which]
     slots, Xe, ids1, w1, dYe = expert_subproblem(r, e)
     gu, dn = expert_fetch(r)(e)
     got = {}
@@ -125,9 +137,11 @@ def check_sampled_expert(r, which):
                                    wl.layout, wl.limit, wl.alpha, dw_sink=lambda i, a, b: got.__setitem__(i, (a, b)))
     ref_gu, ref_dn = got[0]
     g_gu, g_dn = host(r["dgu"][e]), host(r["dd"][e])
-    for half, g, ref in zip(["gate", "up"], halves(g_gu, wl.layout), halves(ref_gu, wl.layout)):
-        assert_parity(g, ref, f"{name} dW_{half}[{e}] ({counts[e]} slots)", stored_bf16=True)
-    assert_parity(g_dn, ref_dn, f"{name} dW_down[{e}] ({counts[e]} slots)", stored_bf16=True)
+    dz, xs, dys, wa = slot_factors(Xe, w1, dYe, gu, dn, wl.act, wl.layout, wl.limit, wl.alpha)
+    for half, g, ref, P in zip(["gate", "up"], halves(g_gu, wl.layout), halves(ref_gu, wl.layout),
+                               oracle.split_gate_up(dz, wl.layout)):
+        assert_parity_slots(g, ref, P, xs, f"{name} dW_{half}[{e}] ({counts[e]} slots)")
+    assert_parity_slots(g_dn, ref_dn, dys, wa, f"{name} dW_down[{e}] ({counts[e]} slots)")
     assert_parity(host(r["dw"]).ravel()[slots], dW.ravel(), f"{name} d_topk_weights of expert {e}", stored_bf16=True)
 
 
@@ -151,3 +165,26 @@ def test_zipf_empty_or_cold_experts_and_shapes():
     for e in np.nonzero(counts == 0)[0]:
         assert torch.count_nonzero(r["dgu"][e]) == 0 and torch.count_nonzero(r["dd"][e]) == 0
     assert torch.isfinite(r["out"]).all() and torch.isfinite(r["dh"]).all()
+
+
+@pytest.mark.parametrize("name,T", [("gptoss", 1), ("gptoss", 37), ("large", 1), ("large", 16), ("large", 2048),
+                                    ("backward", 5), ("backward", 300)])
+def test_small_token_counts_at_full_shapes(name, T):
+    """The layer shapes at token counts from 1 up: most experts empty, a few
+    with one or two slots, every M-tile a ragged tail."""
+    r = run_workload(name, T=T)
+    wl = r["wl"]
+    toks = np.arange(T) if T <= 4 else sample_tokens(r, 4, seed=3)
+    ex = oracle.expert_accessor(expert_fetch(r))
+    ref = oracle.forward(r["X"][toks], r["ids"][toks], r["w"][toks], ex, wl.E, wl.act, wl.layout, wl.limit, wl.alpha)
+    assert_parity(host(r["out"][toks]), ref, f"{name} T={T} out", stored_bf16=True)
+    dX, dW, _, _ = oracle.backward(r["X"][toks], r["ids"][toks], r["w"][toks], r["dY"][toks], ex, wl.E, wl.act,
+                                   wl.layout, wl.limit, wl.alpha, dw_sink=lambda *a: None)
+    assert_parity(host(r["dh"][toks]), dX, f"{name} T={T} d_hidden", stored_bf16=True)
+    assert_parity(host(r["dw"][toks]), dW, f"{name} T={T} d_topk_weights", stored_bf16=True)
+    for which in ("coldest", "median", "hottest"):
+        check_sampled_expert(r, which)
+    counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
+    empty = torch.from_numpy(np.nonzero(counts == 0)[0]).cuda()
+    assert int(torch.count_nonzero(r["dgu"].index_select(0, empty))) == 0
+    assert int(torch.count_nonzero(r["dd"].index_select(0, empty))) == 0

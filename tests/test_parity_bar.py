@@ -1,0 +1,116 @@
+"""The weight-gradient parity bar against a CPU emulation of bf16 rounding.
+
+The emulation follows one expert's weight gradient through the roundings a
+bf16 implementation makes: Z, the activation and its derivative in fp32, the
+GEMM operands (dZ and w*a) rounded to bf16, fp32 sums, the result stored as
+bf16.  The bar must
+accept that chain at every slot count, including one slot, where the block
+is a rank-one matrix with entries of 30+ rms, and must reject plausible
+mistakes: a dropped slot, a tile shifted by one column, a tile that is wrong
+by a few percent of its scale, operands kept at 4 mantissa bits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import bf16_bits_to_f32, f32_to_bf16_bits
+from tests._gpu import assert_parity, assert_parity_slots, slot_factors
+
+H, I = 1024, 512
+
+
+def bf(x):
+    return bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(x, dtype=np.float32))).astype(np.float64)
+
+
+def coarse(x, bits=4):
+    """Round to `bits` mantissa bits (a far too coarse operand format)."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(m * 2.0 ** bits) / 2.0 ** bits, e)
+
+
+def expert(c, act, layout, seed):
+    rng = np.random.default_rng(seed)
+    X = bf(rng.standard_normal((c, H)))
+    gu = bf(rng.standard_normal((2 * I, H)) * 0.02)
+    dn = bf(rng.standard_normal((H, I)) * 0.02)
+    dY = bf(rng.standard_normal((c, H)))
+    w = rng.random((c, 1)).astype(np.float32).astype(np.float64)
+    return X, gu, dn, dY, w
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def bf16_chain(X, gu, dn, dY, w, act, layout, operand=bf):
+    """dW_gate_up and dW_down as the bf16 chain computes them (Z kept in fp32)."""
+    Z = f32(X @ gu.T)
+    g, u = oracle.split_gate_up(Z, layout)
+    a = oracle.glu(g, u, act).astype(np.float32).astype(np.float64)
+    dA = (w * (dY @ dn)).astype(np.float32).astype(np.float64)
+    dg, du = oracle.glu_backward(g, u, dA, act)
+    dz = operand(oracle.merge_gate_up(dg, du, layout).astype(np.float32))
+    wa = operand((w * a).astype(np.float32))
+    return bf((dz.T @ X).astype(np.float32)), bf((dY.T @ wa).astype(np.float32))
+
+
+def reference(X, gu, dn, dY, w, act, layout):
+    dz, xs, dys, wa = slot_factors(X, w, dY, gu, dn, act, layout, 7.0, 1.702)
+    return dz.T @ xs, dys.T @ wa, (dz, xs, dys, wa)
+
+
+def check(got_gu, got_dn, ref_gu, ref_dn, f, layout):
+    dz, xs, dys, wa = f
+    for P, G, R in zip(oracle.split_gate_up(dz, layout), oracle.split_gate_up(got_gu.T, layout),
+                       oracle.split_gate_up(ref_gu.T, layout)):
+        assert_parity_slots(G.T, R.T, P, xs, "dW_gate_up half")
+    assert_parity_slots(got_dn, ref_dn, dys, wa, "dW_down")
+
+
+CASES = [(c, act, layout) for c in (1, 2, 8, 64, 512)
+         for act, layout in (("clamped", "interleaved"), ("swiglu", "concat"))]
+
+
+@pytest.mark.parametrize("c,act,layout", CASES)
+def test_bf16_chain_meets_the_bar(c, act, layout):
+    for seed in range(2):
+        X, gu, dn, dY, w = expert(c, act, layout, seed)
+        ref_gu, ref_dn, f = reference(X, gu, dn, dY, w, act, layout)
+        got_gu, got_dn = bf16_chain(X, gu, dn, dY, w, act, layout)
+        check(got_gu, got_dn, ref_gu, ref_dn, f, layout)
+
+
+def test_plain_floor_is_out_of_reach_with_one_slot():
+    """Why the slot floor exists: the same correct chain fails the plain bf16
+    floor on a one-slot expert."""
+    failed = 0
+    for seed in range(4):
+        X, gu, dn, dY, w = expert(1, "swiglu", "concat", seed)
+        ref_gu, _, _ = reference(X, gu, dn, dY, w, "swiglu", "concat")
+        got_gu, _ = bf16_chain(X, gu, dn, dY, w, "swiglu", "concat")
+        try:
+            assert_parity(got_gu, ref_gu, "dW_gate_up", stored_bf16=True)
+        except AssertionError:
+            failed += 1
+    assert failed > 0
+
+
+@pytest.mark.parametrize("mistake", ["dropped slot", "shifted tile", "tile off by 6%", "4-bit operands"])
+def test_planted_mistakes_fail(mistake):
+    c, act, layout = 64, "swiglu", "concat"
+    X, gu, dn, dY, w = expert(c, act, layout, 11)
+    ref_gu, ref_dn, f = reference(X, gu, dn, dY, w, act, layout)
+    if mistake == "dropped slot":
+        got_gu, got_dn = bf16_chain(X[1:], gu, dn, dY[1:], w[1:], act, layout)
+    elif mistake == "4-bit operands":
+        got_gu, got_dn = bf16_chain(X, gu, dn, dY, w, act, layout, operand=coarse)
+    else:
+        got_gu, got_dn = bf16_chain(X, gu, dn, dY, w, act, layout)
+        rms = np.sqrt(np.mean(got_dn ** 2))
+        if mistake == "shifted tile":
+            got_dn[128:256, 128:256] = got_dn[128:256, 129:257]
+        else:
+            got_dn[128:256, 128:256] += 0.06 * rms
+    with pytest.raises(AssertionError):
+        check(got_gu, got_dn, ref_gu, ref_dn, f, layout)
