@@ -112,12 +112,22 @@ struct Cfg {
   static constexpr int KSTEP = sizeof(T) == 2 ? 16 : 2;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * (int)sizeof(T);
+  // workgroups per CU the launch bounds ask for: two while both fit in LDS
+  static constexpr int OCC = LDS_BYTES > 80 * 1024 ? 1 : 2;
   static_assert((CPR & (CPR - 1)) == 0, "chunks per row must be a power of two");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   __device__ static __forceinline__ int lds_off(int row, int chunk) {
     return row * BK + ((chunk ^ ((row / RPW) & (SW - 1))) * VEC);
   }
 };
+
+// v if ok, else zeros, as bitwise ANDs: a select on a condition shared by all
+// of a thread's chunks is otherwise compiled into a divergent branch, which
+// splits the k-step into basic blocks the scheduler cannot interleave.
+__device__ __forceinline__ uint4 masked(uint4 v, bool ok) {
+  const uint32_t m = 0u - (uint32_t)ok;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
 
 // K-contiguous operand: tile rows are m (or n), each row a contiguous run of k.
 // Every load is issued unconditionally (an out-of-range chunk reads its row's
@@ -129,6 +139,7 @@ struct RowLoader {
   static constexpr int ITEMS = ROWS * C::CPR;
   static constexpr int NI = (ITEMS + C::NT - 1) / C::NT;
   static constexpr bool ALL_ON = ITEMS % C::NT == 0;
+  static constexpr int WRITES = NI;   // LDS stores per step
   const T* rowp[NI];
   int koff[NI];
   int loff[NI];
@@ -166,7 +177,7 @@ struct RowLoader {
   __device__ __forceinline__ void store(T* lds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      if (on[i]) *(uint4*)(lds + loff[i]) = okm[SET][i] ? reg[SET][i] : make_uint4(0, 0, 0, 0);
+      if (on[i]) *(uint4*)(lds + loff[i]) = masked(reg[SET][i], okm[SET][i]);
   }
 };
 
@@ -263,6 +274,7 @@ struct NLoader {
   static constexpr int COLS = 128, CPRN = COLS / 8;
   static constexpr int ITEMS = C::BK * CPRN;
   static constexpr int NI = (ITEMS + C::NT - 1) / C::NT;
+  static constexpr int WRITES = NI;   // LDS stores per step
   int kr[NI], col[NI], loff[NI];
   bool on[NI], col_ok[NI];
   uint4 reg[2][NI];
@@ -304,7 +316,7 @@ struct NLoader {
   __device__ __forceinline__ void store(T* lds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      if (on[i]) *(uint4*)(lds + loff[i]) = okm[SET][i] ? reg[SET][i] : make_uint4(0, 0, 0, 0);
+      if (on[i]) *(uint4*)(lds + loff[i]) = masked(reg[SET][i], okm[SET][i]);
   }
 };
 
@@ -420,6 +432,87 @@ __device__ __forceinline__ void mainloop_pf1(AL& al, BL& bl, ALoadFn aload, BLoa
   }
 }
 
+// Fragments of one 16-wide k-slice of a wave's tile (bf16).
+template <class C>
+struct KFrags {
+  bf16x8_t a[C::FM], b[C::FN];
+};
+
+template <class C, bool A_N, bool B_N>
+__device__ __forceinline__ void read_kfrags(const typename C::elem* As, const typename C::elem* Bs, int kk,
+                                            KFrags<C>& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r32 = lane & 31, chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = A_N ? frag_n<C>(As, wm * C::WTM + fm * 32, kk, lane)
+                  : *(const bf16x8_t*)(As + C::lds_off(wm * C::WTM + fm * 32 + r32, chunk));
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+    f.b[fn] = B_N ? frag_n<C>(Bs, wn * C::WTN + fn * 32, kk, lane)
+                  : *(const bf16x8_t*)(Bs + C::lds_off(wn * C::WTN + fn * 32 + r32, chunk));
+}
+
+template <class C>
+__device__ __forceinline__ void mma_kfrags(const KFrags<C>& f, f32x16 (&acc)[C::FM][C::FN]) {
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fm][fn], 0, 0, 0);
+}
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+enum : int { kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200 };
+
+// One k-step of the bf16 pipeline (LDS buffers As/Bs hold step kt).  Global
+// loads go to register set SET; the next LDS stage is stored from STORE_SET:
+// with two sets, SET receives step kt+2 while the other set (loaded a step
+// ago) holds step kt+1; with one set, SET = STORE_SET receives step kt+1 and is
+// stored at the end of the same step.  The k-slices are
+// software-pipelined: slice kk+1's fragments are read from LDS while slice
+// kk's MFMAs run, so LDS latency is exposed once per step instead of once per
+// slice, and the next stage's LDS stores (which only wait for loads issued a
+// step ago) and this step's global loads are spread between the MFMAs.
+template <class C, bool A_N, bool B_N, int SET, int STORE_SET, class AL, class BL, class ALoadFn, class BLoadFn>
+__device__ __forceinline__ void pipelined_step(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int kload,
+                                               const typename C::elem* As, const typename C::elem* Bs,
+                                               typename C::elem* As_next, typename C::elem* Bs_next,
+                                               f32x16 (&acc)[C::FM][C::FN]) {
+  constexpr int KK = C::BK / C::KSTEP;
+  constexpr int READS = C::FM * (A_N ? 2 : 1) + C::FN * (B_N ? 2 : 1);   // LDS reads per slice
+  constexpr int MFMAS = C::FM * C::FN;                                   // per slice
+  constexpr int LOADS = AL::NI + BL::NI;                                 // global loads per step
+  constexpr int WRITES = AL::WRITES + BL::WRITES;                        // LDS stores per step
+  static_assert(KK >= 2, "at least two k-slices per step");
+  KFrags<C> f[2];
+  read_kfrags<C, A_N, B_N>(As, Bs, 0, f[0]);
+  aload(al, kload, Set<SET>{});
+  bload(bl, kload, Set<SET>{});
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + 1 < KK) read_kfrags<C, A_N, B_N>(As, Bs, kk + 1, f[(kk + 1) & 1]);
+    mma_kfrags<C>(f[kk & 1], acc);
+  }
+  al.template store<STORE_SET>(As_next);
+  bl.template store<STORE_SET>(Bs_next);
+  // order: slice 0 reads, global loads, then per slice the next slice's reads
+  // followed by its MFMAs with this step's LDS stores spread between them
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, LOADS, 0);
+  constexpr int WPS = (WRITES + KK - 2) / (KK - 1);   // LDS stores per slice after the first
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+#pragma unroll
+    for (int m = 0; m < MFMAS; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (kk >= 1 && m < WPS) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+    }
+  }
+}
+
 template <class C, bool A_N = false, bool B_N = false, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                          typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
@@ -436,8 +529,9 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
   T* Bs0 = lds + 2 * C::A_ELEMS;
   T* Bs1 = Bs0 + C::B_ELEMS;
   // Every prefetch is issued, clamped to the last step (a redundant reload of
-  // a tile that is still in L2), so the number of loads in flight does not
-  // depend on a branch and the LDS stores of one set wait only for that set.
+  // a tile that is still in L2), and every step stores the next stage (after
+  // the last step into the buffer nothing reads again), so a step is one
+  // basic block whose loads in flight do not depend on a branch.
   const int last = nk - 1;
   aload(al, 0, Set<0>{});
   bload(bl, 0, Set<0>{});
@@ -448,23 +542,11 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
   __syncthreads();
   for (int kt = 0;;) {
     // even step: LDS buffer 0 holds step kt, register set 1 holds step kt+1
-    aload(al, min(kt + 2, last), Set<0>{});
-    bload(bl, min(kt + 2, last), Set<0>{});
-    mma_tile<C, A_N, B_N>(As0, Bs0, acc);
-    if (kt + 1 < nk) {
-      al.template store<1>(As1);
-      bl.template store<1>(Bs1);
-    }
+    pipelined_step<C, A_N, B_N, 0, 1>(al, bl, aload, bload, min(kt + 2, last), As0, Bs0, As1, Bs1, acc);
     __syncthreads();
     if (++kt >= nk) break;
     // odd step: LDS buffer 1 holds step kt, register set 0 holds step kt+1
-    aload(al, min(kt + 2, last), Set<1>{});
-    bload(bl, min(kt + 2, last), Set<1>{});
-    mma_tile<C, A_N, B_N>(As1, Bs1, acc);
-    if (kt + 1 < nk) {
-      al.template store<0>(As0);
-      bl.template store<0>(Bs0);
-    }
+    pipelined_step<C, A_N, B_N, 1, 0>(al, bl, aload, bload, min(kt + 2, last), As1, Bs1, As0, Bs0, acc);
     __syncthreads();
     if (++kt >= nk) break;
   }
@@ -546,23 +628,25 @@ template <class C, int ROT>
 using MNLoader = std::conditional_t<sizeof(typename C::elem) == 2, NLoader<C, ROT>, TransLoader<C, 128, ROT>>;
 template <class C> constexpr bool kNLayout = sizeof(typename C::elem) == 2;
 
-// bf16 operands fit two register sets in 256 VGPRs up to 128-row tiles;
-// 192-row tiles and fp32 operands use one.
+// bf16 operands fit the two-set pipeline in 256 registers up to 128-row
+// tiles; taller tiles and fp32 operands use the one-set loop.
+template <class C>
+constexpr bool kTwoSets = sizeof(typename C::elem) == 2 && C::BM <= 128;
 template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop_rows(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                               typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
-  if constexpr (sizeof(typename C::elem) == 2 && C::BM <= 128) mainloop<C>(al, bl, aload, bload, nk, lds, acc);
+  if constexpr (kTwoSets<C>) mainloop<C>(al, bl, aload, bload, nk, lds, acc);
   else mainloop_pf1<C>(al, bl, aload, bload, nk, lds, acc);
 }
 
 // ---------------------------------------------------------------- gate_up fwd
 // Local B rows: 32-row groups alternate gate and up rows of the same 32
-// activation columns, so the fn = 0 and fn = 1 fragments of a wave hold
-// matching g and u values.
+// activation columns, so the fn = 2p and fn = 2p+1 fragments of a wave hold
+// matching g and u values (activation columns (wn*FN/2 + p)*32 + 0..31).
 template <class C, bool WRITE_A, bool WRITE_Z>
-__global__ __launch_bounds__(C::NT, 2) void gate_up_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, C::OCC) void gate_up_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
-  static_assert(C::FN == 2 && C::WTN == 64, "gate/up pairing assumes 64-column wave tiles");
+  static_assert(C::FN % 2 == 0, "gate/up pairing needs an even number of 32-column fragments");
   int e, m0, rows, nt;
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I = g.I;
@@ -595,14 +679,16 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_kernel(GArgs g) {
     if (rl >= rows) continue;
     const size_t p = (size_t)(m0 + rl);
 #pragma unroll
+    for (int pr = 0; pr < C::FN / 2; ++pr)
+#pragma unroll
     for (int vg = 0; vg < 4; ++vg) {
-      const int j = j0 + wn * 32 + acc_col4(vg, lane);
+      const int j = j0 + (wn * (C::FN / 2) + pr) * 32 + acc_col4(vg, lane);
       if (j >= I) continue;
       float gv[4], uv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        gv[i] = acc[fm][0][vg * 4 + i];
-        uv[i] = acc[fm][1][vg * 4 + i];
+        gv[i] = acc[fm][2 * pr][vg * 4 + i];
+        uv[i] = acc[fm][2 * pr + 1][vg * 4 + i];
       }
       if (WRITE_A)
         store4<T>(a_out + p * I + j, glu_fwd(gv[0], uv[0], g.act, g.limit, g.alpha),
@@ -623,7 +709,7 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_kernel(GArgs g) {
 
 // ---------------------------------------------------------------- down fwd
 template <class C>
-__global__ __launch_bounds__(C::NT, 2) void down_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, C::OCC) void down_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   int e, m0, rows, nt;
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
@@ -662,7 +748,7 @@ __global__ __launch_bounds__(C::NT, 2) void down_kernel(GArgs g) {
 // r[p, i] = sum_h dYp[p, h] * Wd[e][h, i]; epilogue: a = phi(Z), partial
 // <r, a> per row for dTopkW, da = w r, dZ = phi'(Z) da, aw = w a.
 template <class C>
-__global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, C::OCC) void down_dgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   int e, m0, rows, nt;
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
@@ -679,8 +765,9 @@ __global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
   auto bload = [&](auto& l, int kt, auto set) {
     l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * I + n0; });
   };
-  if constexpr (kNLayout<C> && C::BM <= 128) mainloop<C, false, true>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
-  else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, (H + C::BK - 1) / C::BK, lds, acc);
+  const int nk = (H + C::BK - 1) / C::BK;
+  if constexpr (kTwoSets<C>) mainloop<C, false, true>(al, bl, aload, bload, nk, lds, acc);
+  else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, nk, lds, acc);
 
   const float* Z = (const float*)g.Z;
   T* dZ = (T*)g.out0;
@@ -743,7 +830,7 @@ __global__ __launch_bounds__(C::NT, 2) void down_dgrad_kernel(GArgs g) {
 // ---------------------------------------------------------------- gate_up dgrad
 // dXp[p, h] = sum_j dZ[p, j] * Wgu[e][j, h]
 template <class C>
-__global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
+__global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   int e, m0, rows, nt;
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
@@ -760,8 +847,9 @@ __global__ __launch_bounds__(C::NT, 2) void gate_up_dgrad_kernel(GArgs g) {
   auto bload = [&](auto& l, int kt, auto set) {
     l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * H + n0; });
   };
-  if constexpr (kNLayout<C> && C::BM <= 128) mainloop<C, false, true>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
-  else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, (I2 + C::BK - 1) / C::BK, lds, acc);
+  const int nk = (I2 + C::BK - 1) / C::BK;
+  if constexpr (kTwoSets<C>) mainloop<C, false, true>(al, bl, aload, bload, nk, lds, acc);
+  else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, nk, lds, acc);
   float* dXp = (float*)g.out0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
