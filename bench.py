@@ -257,11 +257,51 @@ PROTOCOL = [("gptoss", "fwd", False), ("gptoss", "fwd", True), ("gptoss", "bwd",
             ("zipf", "fwd", True), ("zipf", "fwd", False), ("zipf", "bwd", True), ("zipf", "bwd", False)]
 
 
+def router_record(wl, dev, warmup, iters, seed=0):
+    """Time moe_router on the workload's router logits (fp32 [T,E]) and, for
+    comparison, moe_route on the ids it produces, each iteration after a
+    512 MiB cache flush.  Algorithmic bytes: logits in, ids and weights out,
+    the slot permutation and its inverse out."""
+    import numpy as np
+    import torch
+    import mixture_experts_expert_histogram_amd as moe
+    from synth import router_logits
+    lg = torch.from_numpy(router_logits(wl.T, wl.E, seed)).to(dev)
+    flush = torch.empty(PassRunner.FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    d = moe.make_desc(wl.T, 8, 8, wl.E, wl.K)
+    ws = moe.empty_workspace(moe.route_workspace_size(d), dev)
+    ids = torch.empty((wl.T, wl.K), dtype=torch.int32, device=dev)
+    w = torch.empty((wl.T, wl.K), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            flush.fill_(1)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    t_router = timed(lambda: moe.router(lg, wl.K, ws=ws, out=(ids, w)))
+    t_route = timed(lambda: moe.route(ids, wl.E, ws=ws))
+    if moe.check_device_status(ws) != 0:
+        raise RuntimeError("bad expert id reported by the device")
+    nbytes = wl.T * wl.E * 4 + wl.S * 8 + wl.S * 8
+    return {"workload": wl.name, "pass": "router", "T": wl.T, "E": wl.E, "K": wl.K,
+            "router_median_us": round(t_router, 2), "route_from_ids_median_us": round(t_route, 2),
+            "algorithmic_mb": round(nbytes / 1e6, 3), "router_gbps": round(nbytes / (t_router * 1e-6) / 1e9, 1)}
+
+
 def run_protocol(args):
     import torch
     from synth import WORKLOADS
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    for name in ("gptoss", "large", "backward", "zipf"):
+        print(json.dumps(router_record(WORKLOADS[name], dev, args.warmup, args.iters)), flush=True)
     current, runner = None, None
     for name, pass_, saved in PROTOCOL:
         if name != current:

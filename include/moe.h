@@ -112,6 +112,31 @@ moe_status_t moe_route(const moe_desc_t* desc, const int32_t* topk_ids,
                        int32_t* inv_pos, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Router + routing in one pipeline.  The pages take the top-k expert ids and
+ * weights as inputs of the layer ("MoE expert parallel execution backward"
+ * lists topk_weights among the tensors it differentiates); this produces
+ * them from router logits the way the workloads define routing: the softmax
+ * over a token's E logits, its K largest entries, renormalised to sum to one
+ * (equal, up to rounding, to the softmax of the K largest logits).
+ *   logits        fp32 [T,E] (read only; finite values expected: an infinite
+ *                 logit can give NaN weights, and a token whose remaining
+ *                 logits are all NaN gets id -1 in the slots left, reported
+ *                 as MOE_ERR_BAD_EXPERT_ID by moe_check_device_status)
+ *   topk_ids      int32 [T,K] out: ids by descending logit; equal logits in
+ *                 ascending id (bit-exact: ids are decided by comparisons of
+ *                 the fp32 logits only)
+ *   topk_weights  fp32 [T,K] out: exp(l_k - l_0) / sum_j exp(l_j - l_0) in
+ *                 fp32, summed in k order (a few ulp from the exact value)
+ *   counts, offsets, sorted_slot, inv_pos: as moe_route for these ids (each
+ *                 may be NULL).
+ * Requires K <= E (else MOE_ERR_INVALID_ARG).  ws: at least
+ * moe_route_workspace_size() bytes; the routing it leaves there is the one
+ * moe_fwd would compute from topk_ids. */
+moe_status_t moe_router(const moe_desc_t* desc, const float* logits,
+                        int32_t* topk_ids, float* topk_weights, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slot, int32_t* inv_pos,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Forward: out [T,H] = sum_k w[t,k] * FFN_{ids[t,k]}(hidden[t]).
  * Routing, gate_up projection with the gated activation, down projection with
  * the routing weight, and a deterministic per-token sum over the K slots
@@ -136,6 +161,27 @@ moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden,
                      const void* d_out, const void* saved, void* d_hidden,
                      float* d_topk_weights, void* d_w_gate_up, void* d_w_down,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Forward from router logits [T,E] (fp32): moe_router's top-k and weights
+ * (written to topk_ids [T,K] and topk_weights [T,K] for the backward), then
+ * moe_fwd on them in the same call.  Same outputs, workspace, `saved` and
+ * errors as moe_fwd (plus K <= E). */
+moe_status_t moe_fwd_logits(const moe_desc_t* desc, const void* hidden,
+                            const float* logits, const void* w_gate_up,
+                            const void* w_down, void* out, int32_t* topk_ids,
+                            float* topk_weights, void* saved, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Gradient of the router's weights with respect to its logits, given
+ * d_topk_weights fp32 [T,K] (from moe_bwd): d_logits fp32 [T,E] with
+ *   d_logits[t, ids[t,k]] = w[t,k] * (g[t,k] - sum_j w[t,j] g[t,j])
+ * and zero for experts not chosen (the choice is piecewise constant in the
+ * logits).  Ids outside [0,E) contribute nothing; a repeated id of one token
+ * receives the sum of its terms.  fp32, one writer per element. */
+moe_status_t moe_router_bwd(const moe_desc_t* desc, const int32_t* topk_ids,
+                            const float* topk_weights,
+                            const float* d_topk_weights, float* d_logits,
+                            hipStream_t stream);
 
 /* Synchronises `stream` and reports MOE_ERR_BAD_EXPERT_ID if the last
  * routing done in `ws` met an id outside [0,E), else MOE_OK. */

@@ -18,9 +18,9 @@ MOE_BF16, MOE_F32 = 0, 1
 MOE_SWIGLU, MOE_CLAMPED_GLU = 0, 1
 MOE_GU_CONCAT, MOE_GU_INTERLEAVED = 0, 1
 
-EXPORTED = ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_fwd", "moe_bwd",
-            "moe_check_device_status", "moe_status_str", "moe_timing_enable", "moe_timing_disable",
-            "moe_timing_read"]
+EXPORTED = ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_router", "moe_fwd",
+            "moe_fwd_logits", "moe_bwd", "moe_router_bwd", "moe_check_device_status", "moe_status_str",
+            "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]
 
 
 class MoeDesc(ctypes.Structure):
@@ -59,7 +59,10 @@ def library() -> ctypes.CDLL:
     lib.moe_workspace_size.argtypes = [pd, psz, psz, psz]
     lib.moe_route_workspace_size.argtypes = [pd, psz]
     lib.moe_route.argtypes = [pd, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_router.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_fwd_logits.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_router_bwd.argtypes = [pd, vp, vp, vp, vp, vp]
     lib.moe_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_check_device_status.argtypes = [vp, vp]
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -67,8 +70,9 @@ def library() -> ctypes.CDLL:
     lib.moe_timing_enable.argtypes = [ctypes.c_int32]
     lib.moe_timing_disable.argtypes = []
     lib.moe_timing_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
-    for name in ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_fwd", "moe_bwd",
-                 "moe_check_device_status", "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]:
+    for name in ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_router", "moe_fwd",
+                 "moe_fwd_logits", "moe_bwd", "moe_router_bwd", "moe_check_device_status", "moe_timing_enable",
+                 "moe_timing_disable", "moe_timing_read"]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -169,6 +173,66 @@ def route(topk_ids, E: int, ws=None):
     _check(library().moe_route(ctypes.byref(d), _ptr(ids), _ptr(counts), _ptr(offsets), _ptr(ss), _ptr(ip),
                                _ptr(ws), ws.numel(), _stream()), "moe_route")
     return counts, offsets, ss, ip, ws
+
+
+def router(logits, K: int, ws=None, out=None):
+    """Top-K of router logits [T,E] (fp32) and their softmax, with the routing.
+
+    Returns (topk_ids int32 [T,K], topk_weights fp32 [T,K], counts [E],
+    offsets [E+1], sorted_slot [S], inv_pos [S], ws)."""
+    import torch
+    lg = _f32(logits)
+    T, E = lg.shape
+    d = make_desc(T, 8, 8, E, K)
+    dev = lg.device
+    ws = empty_workspace(route_workspace_size(d), dev) if ws is None else ws
+    if out is None:
+        out = (torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.float32, device=dev))
+    ids, w = out
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ss = torch.empty(T * K, dtype=torch.int32, device=dev)
+    ip = torch.empty(T * K, dtype=torch.int32, device=dev)
+    _check(library().moe_router(ctypes.byref(d), _ptr(lg), _ptr(ids), _ptr(w), _ptr(counts), _ptr(offsets),
+                                _ptr(ss), _ptr(ip), _ptr(ws), ws.numel(), _stream()), "moe_router")
+    return ids, w, counts, offsets, ss, ip, ws
+
+
+def router_bwd(topk_ids, topk_weights, d_topk_weights, E: int, out=None):
+    """d_logits fp32 [T,E] from the routing-weight gradient."""
+    import torch
+    ids, w, g = _ids32(topk_ids), _f32(topk_weights), _f32(d_topk_weights)
+    T, K = ids.shape
+    d = make_desc(T, 8, 8, E, K)
+    out = torch.empty((T, E), dtype=torch.float32, device=ids.device) if out is None else out
+    _check(library().moe_router_bwd(ctypes.byref(d), _ptr(ids), _ptr(w), _ptr(g), _ptr(out), _stream()),
+           "moe_router_bwd")
+    return out
+
+
+def fwd_logits(hidden, logits, K: int, w_gate_up, w_down, act="swiglu", layout="concat", limit=7.0, alpha=1.702,
+               save=False, ws=None, out=None, saved=None, routing=None):
+    """Forward from router logits [T,E]; returns (out, topk_ids, topk_weights, saved-or-None, ws)."""
+    import torch
+    lg = _f32(logits)
+    T, E = lg.shape
+    if T != hidden.shape[0] or E != w_gate_up.shape[0]:
+        raise ValueError("logits must be [T, E] for hidden [T, H] and w_gate_up [E, 2I, H]")
+    dev = hidden.device
+    if routing is None:
+        routing = (torch.empty((T, K), dtype=torch.int32, device=dev),
+                   torch.empty((T, K), dtype=torch.float32, device=dev))
+    ids, w = routing
+    d = _desc_for(hidden, ids, w_gate_up, w_down, act, layout, limit, alpha)
+    fws, _, sbytes = workspace_size(d)
+    ws = empty_workspace(fws, dev) if ws is None else ws
+    out = torch.empty_like(hidden) if out is None else out
+    if save and saved is None:
+        saved = empty_workspace(sbytes, dev)
+    _check(library().moe_fwd_logits(ctypes.byref(d), _ptr(hidden), _ptr(lg), _ptr(w_gate_up), _ptr(w_down),
+                                    _ptr(out), _ptr(ids), _ptr(w), _ptr(saved) if save else None, _ptr(ws),
+                                    ws.numel(), _stream()), "moe_fwd_logits")
+    return out, ids, w, (saved if save else None), ws
 
 
 def fwd(hidden, topk_ids, topk_weights, w_gate_up, w_down, act="swiglu", layout="concat", limit=7.0,

@@ -223,15 +223,87 @@ moe_status_t moe_route(const moe_desc_t* desc, const int32_t* topk_ids, int32_t*
   return MOE_OK;
 }
 
+moe_status_t moe_router(const moe_desc_t* desc, const float* logits, int32_t* topk_ids, float* topk_weights,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* inv_pos, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  Dims d;
+  moe_status_t st = check_desc(desc, &d);
+  if (st != MOE_OK) return st;
+  if (d.K > d.E || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {logits, topk_ids, topk_weights, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(d);
+  if (ws_bytes < L.route_end) return MOE_ERR_WORKSPACE;
+  RouteState rs = route_state(ws, L, d);
+  if (d.T == 0) {
+    HIP_TRY(launch_fill_zero((char*)ws + L.status, 4 * sizeof(int32_t), stream));
+  } else {
+    HIP_TRY(launch_route_logits(logits, (int)d.T, (int)d.K, (int)d.E, topk_ids, topk_weights, rs, stream));
+  }
+  if (counts) {
+    if (d.T == 0) HIP_TRY(launch_fill_zero(counts, d.E * 4, stream));
+    else HIP_TRY(hipMemcpyAsync(counts, rs.counts, d.E * 4, hipMemcpyDeviceToDevice, stream));
+  }
+  if (offsets) {
+    if (d.T == 0) HIP_TRY(launch_fill_zero(offsets, (d.E + 1) * 4, stream));
+    else HIP_TRY(hipMemcpyAsync(offsets, rs.offsets, (d.E + 1) * 4, hipMemcpyDeviceToDevice, stream));
+  }
+  if (sorted_slot && d.S)
+    HIP_TRY(hipMemcpyAsync(sorted_slot, rs.sorted_slot, d.S * 4, hipMemcpyDeviceToDevice, stream));
+  if (inv_pos && d.S) HIP_TRY(hipMemcpyAsync(inv_pos, rs.inv_pos, d.S * 4, hipMemcpyDeviceToDevice, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_router_bwd(const moe_desc_t* desc, const int32_t* topk_ids, const float* topk_weights,
+                            const float* d_topk_weights, float* d_logits, hipStream_t stream) {
+  Dims d;
+  moe_status_t st = check_desc(desc, &d);
+  if (st != MOE_OK) return st;
+  if (d.T > 0 && (!topk_ids || !topk_weights || !d_topk_weights || !d_logits)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {topk_ids, topk_weights, d_topk_weights, d_logits};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  HIP_TRY(launch_router_bwd(topk_ids, topk_weights, d_topk_weights, (int)d.T, (int)d.E, (int)d.K, d_logits,
+                            stream));
+  return MOE_OK;
+}
+
+static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, const float* logits, int32_t* ids_out, float* w_out,
+                             const void* w_gate_up, const void* w_down, void* out, void* saved, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
 moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                      const float* topk_weights, const void* w_gate_up, const void* w_down, void* out, void* saved,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (desc && desc->T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  return fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate_up, w_down, out, saved,
+                  ws, ws_bytes, stream);
+}
+
+moe_status_t moe_fwd_logits(const moe_desc_t* desc, const void* hidden, const float* logits,
+                            const void* w_gate_up, const void* w_down, void* out, int32_t* topk_ids,
+                            float* topk_weights, void* saved, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (desc && desc->T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  if (desc && desc->K > desc->E) return MOE_ERR_INVALID_ARG;
+  return fwd_impl(desc, hidden, topk_ids, topk_weights, logits, topk_ids, topk_weights, w_gate_up, w_down, out,
+                  saved, ws, ws_bytes, stream);
+}
+
+// Forward from given ids and weights (logits == NULL) or from router logits
+// (ids_out / w_out receive the router's choice).
+static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, const float* logits, int32_t* ids_out, float* w_out,
+                             const void* w_gate_up, const void* w_down, void* out, void* saved, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   Dims d;
   moe_status_t st = check_desc(desc, &d);
   if (st != MOE_OK) return st;
   if (!w_gate_up || !w_down || !ws) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!hidden || !topk_ids || !topk_weights || !out)) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {hidden, topk_ids, topk_weights, w_gate_up, w_down, out, saved, ws};
+  const void* ptrs[] = {hidden, topk_ids, topk_weights, logits, w_gate_up, w_down, out, saved, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
@@ -245,7 +317,10 @@ moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden, const int32_t* 
   char* b = (char*)ws;
   void* a = b + L.f_a;
   float* yp = (float*)(b + L.f_y);
-  HIP_TRY(launch_route(topk_ids, topk_weights, (int)d.S, (int)d.K, (int)d.E, rs, stream));
+  if (logits)
+    HIP_TRY(launch_route_logits(logits, (int)d.T, (int)d.K, (int)d.E, ids_out, w_out, rs, stream));
+  else
+    HIP_TRY(launch_route(topk_ids, topk_weights, (int)d.S, (int)d.K, (int)d.E, rs, stream));
   if (pb.dtype == 0 && lds_dma_engine_enabled()) {
     void* xp = b + L.f_xp;
     HIP_TRY(launch_gather_rows(hidden, rs.tok_of_pos, (int)d.S, d.H * d.esz, xp, stream));

@@ -46,6 +46,12 @@ inline hipError_t run_kernel(const char* name, hipStream_t stream, F&& launch) {
 // ---- routing / combine / reduce (route.hip)
 hipError_t launch_route(const int32_t* ids, const float* w, int S, int K, int E,
                         const RouteState& rs, hipStream_t stream);
+// router: top-K of logits [T,E] and their softmax -> ids, w [T,K]; then as launch_route
+hipError_t launch_route_logits(const float* logits, int T, int K, int E, int32_t* ids, float* w,
+                               const RouteState& rs, hipStream_t stream);
+// d_logits [T,E] from the routing-weight gradient through the softmax over the chosen K
+hipError_t launch_router_bwd(const int32_t* ids, const float* w, const float* dw, int T, int E, int K,
+                             float* d_logits, hipStream_t stream);
 // out[t] = sum_k Yp[inv_pos[t*K+k]] from fp32 rows, stored in dtype
 hipError_t launch_combine(int dtype, const float* Yp, const int32_t* inv_pos, int T, int K, int H,
                           void* out, hipStream_t stream);

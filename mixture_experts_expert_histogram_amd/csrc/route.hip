@@ -171,6 +171,104 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_scatter_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Router: for each token the K largest of its E logits (descending; equal
+// logits in ascending expert id) and, as its routing weights, the softmax of
+// those K logits, which is the softmax over all E logits renormalised over
+// the K chosen.  One wavefront per token, spread over the whole chip: a lane
+// holds logits lane, lane+64, ...; each of K rounds takes the wave-wide best
+// (value, then lower id) of the logits not yet taken.  The histogram, scan
+// and scatter then run on the ids as for given ids.  (Counting the histogram
+// in this kernel instead ties each 2048-slot chunk's tokens to one
+// workgroup, so a 4096-token batch ran on 8 CUs, ~150 us of dependent
+// cross-lane reductions; spread out it is a few microseconds.)  A token whose
+// remaining logits are all NaN gets id -1 in the slots left, which the
+// histogram reports as a bad id.
+namespace {
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+}  // namespace
+
+constexpr int LOGIT_SLOTS = MAX_E / 64;   // logits per lane
+
+__global__ __launch_bounds__(256) void route_logits_kernel(const float* __restrict__ logits, int T, int E, int K,
+                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nj = (E + 63) >> 6;
+  const float* row = logits + (long)t * E;
+  float v[LOGIT_SLOTS];
+  unsigned taken = 0;   // bit j: logit lane + 64 j is chosen or does not exist
+#pragma unroll
+  for (int j = 0; j < LOGIT_SLOTS; ++j) {
+    const int e = lane + 64 * j;
+    const bool ok = j < nj && e < E;
+    v[j] = ok ? row[e] : 0.f;
+    if (!ok) taken |= 1u << j;
+  }
+  float top_z = 0.f, mx = 0.f, denom = 0.f;
+  int top_i = -1;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < LOGIT_SLOTS; ++j)
+      if (!(taken >> j & 1u) && better(v[j], lane + 64 * j, bv, bi)) { bv = v[j]; bi = lane + 64 * j; }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d);
+      const int oi = __shfl_xor(bi, d);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const bool found = bi < E;
+    if (found && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (k == 0) mx = bv;
+    // fp32 softmax of the chosen logits, summed in k order; lane k keeps round k
+    const float z = found ? expf(bv - mx) : 0.f;
+    denom += z;
+    if (lane == k) { top_z = z; top_i = found ? bi : -1; }
+  }
+  if (lane < K) {
+    const long s = (long)t * K + lane;
+    ids[s] = top_i;
+    w[s] = top_i >= 0 ? top_z / denom : 0.f;
+  }
+}
+
+// d_logits[t, ids[t,k]] = w_k (g_k - sum_j w_j g_j), zero elsewhere: the
+// derivative of the softmax over the K chosen logits (the choice itself is
+// piecewise constant).  One wavefront per token, each lane owning logits
+// lane, lane+64, ...; repeated ids of a token add their terms.
+__global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ dw, int T, int E, int K,
+                                                         float* __restrict__ d_logits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t* ti = ids + (long)t * K;
+  const float* tw = w + (long)t * K;
+  const float* tg = dw + (long)t * K;
+  float dot = 0.f;
+  for (int k = 0; k < K; ++k) dot += tw[k] * tg[k];
+  for (int e = lane; e < E; e += 64) {
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k)
+      if (ti[k] == e) acc += tw[k] * (tg[k] - dot);
+    d_logits[(long)t * E + e] = acc;
+  }
+}
+
+hipError_t launch_router_bwd(const int32_t* ids, const float* w, const float* dw, int T, int E, int K,
+                             float* d_logits, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  return run_kernel("router_bwd", stream, [&] {
+    router_bwd_kernel<<<(T + 3) / 4, 256, 0, stream>>>(ids, w, dw, T, E, K, d_logits);
+  });
+}
+
 hipError_t launch_route(const int32_t* ids, const float* w, int S, int K, int E, const RouteState& rs,
                         hipStream_t stream) {
   const int nblk = rs.nblk;
@@ -187,6 +285,15 @@ hipError_t launch_route(const int32_t* ids, const float* w, int S, int K, int E,
     route_scatter_kernel<<<nblk, ROUTE_THREADS, 0, stream>>>(ids, w, S, K, E, rs.blk_hist, rs.sorted_slot,
                                                              rs.inv_pos, rs.tok_of_pos, rs.w_of_pos);
   });
+}
+
+hipError_t launch_route_logits(const float* logits, int T, int K, int E, int32_t* ids, float* w,
+                               const RouteState& rs, hipStream_t stream) {
+  hipError_t err = run_kernel("route_logits", stream, [&] {
+    route_logits_kernel<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, K, ids, w);
+  });
+  if (err != hipSuccess) return err;
+  return launch_route(ids, w, T * K, K, E, rs, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -7,6 +7,6 @@ Python binding) never does, and this package never imports the product.
 See ``oracle.moe`` for the definitions and the passages each one follows.
 """
 from .moe import (  # noqa: F401
-    route, split_gate_up, merge_gate_up, glu, glu_backward,
+    route, router, router_backward, split_gate_up, merge_gate_up, glu, glu_backward,
     expert_accessor, forward, backward, slot_outputs,
 )

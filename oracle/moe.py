@@ -70,6 +70,53 @@ def route(topk_ids: np.ndarray, E: int):
 
 
 # ------------------------------------------------------------------ GLU
+def router(logits: np.ndarray, K: int):
+    """Top-K expert ids and routing weights from router logits [T, E].
+
+    The pages take topk_ids and topk_weights as given inputs ("MoE expert
+    parallel execution backward" differentiates topk_weights).  The routing
+    that produces them is the one the workloads are defined with: the softmax
+    over a token's E logits, its K largest entries, renormalised to sum to
+    one.  Written out in that order, in fp64:
+
+    p = softmax(logits[t])        (max subtracted for range)
+    ids[t] = the K largest, by descending logit (softmax is increasing, so
+             ranking logits ranks p without p's underflow ties); equal
+             logits in ascending expert id
+    w[t, k] = p[ids[t, k]] / sum_j p[ids[t, j]]
+    """
+    lg = np.asarray(logits, dtype=F64)
+    T, E = lg.shape
+    if not 1 <= K <= E:
+        raise ValueError("need 1 <= K <= E")
+    z = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    ids = np.argsort(-lg, axis=1, kind="stable")[:, :K]
+    chosen = np.take_along_axis(p, ids, axis=1)
+    return ids.astype(np.int64), chosen / chosen.sum(axis=1, keepdims=True)
+
+
+def router_backward(topk_ids: np.ndarray, topk_weights: np.ndarray, d_topk_weights: np.ndarray, E: int):
+    """dL/dlogits [T, E] given dL/dw [T, K], by the chain rule on router().
+
+    With the choice held fixed (it is piecewise constant in the logits),
+    w_k = exp(l_{i_k}) / sum_j exp(l_{i_j}), so dw_k/dl_{i_m} =
+    w_k (delta_km - w_m) and dL/dl_{i_m} = w_m (g_m - sum_k w_k g_k); logits
+    not chosen get zero.  A repeated id adds its terms.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(topk_weights, dtype=F64)
+    g = np.asarray(d_topk_weights, dtype=F64)
+    T, K = ids.shape
+    d = np.zeros((T, E), dtype=F64)
+    dot = np.sum(w * g, axis=1)
+    for t in range(T):
+        for k in range(K):
+            if 0 <= ids[t, k] < E:
+                d[t, ids[t, k]] += w[t, k] * (g[t, k] - dot[t])
+    return d
+
+
 def split_gate_up(Z: np.ndarray, layout: str):
     """Split gate_up projection outputs [c, 2I] into gate and up [c, I]."""
     I = Z.shape[1] // 2

@@ -115,9 +115,14 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- routing
+def router_logits(T: int, E: int, seed: int = 0) -> np.ndarray:
+    """The N(0,1) router logits [T,E] (fp32) behind routing_softmax_topk."""
+    return _child(seed, _S_LOGITS).standard_normal((T, E), dtype=np.float32)
+
+
 def routing_softmax_topk(T: int, E: int, K: int, seed: int = 0):
     """Top-k ids and renormalised softmax weights from N(0,1) router logits."""
-    logits = _child(seed, _S_LOGITS).standard_normal((T, E), dtype=np.float32)
+    logits = router_logits(T, E, seed)
     order = np.argsort(-logits, axis=1, kind="stable")[:, :K]
     chosen = np.take_along_axis(logits, order, axis=1).astype(np.float64)
     z = np.exp(chosen - chosen.max(axis=1, keepdims=True))

@@ -92,3 +92,22 @@ def test_route_and_status_argument_errors():
     assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, p, 1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_check_device_status(None, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_timing_enable(0) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_router_argument_errors():
+    lib = moe.library()
+    p = ctypes.c_void_p(16)
+    d = moe.make_desc(64, 8, 8, 8, 2)
+    big = 1 << 30
+    # K > E: the router cannot pick K distinct experts
+    d9 = moe.make_desc(64, 8, 8, 8, 9)
+    assert lib.moe_router(ctypes.byref(d9), p, p, p, None, None, None, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_router(ctypes.byref(d), None, p, p, None, None, None, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_router(ctypes.byref(d), ctypes.c_void_p(8), p, p, None, None, None, None, p, big,
+                          None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_router(ctypes.byref(d), p, p, p, None, None, None, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_fwd_logits(ctypes.byref(d), p, None, p, p, p, p, p, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd_logits(ctypes.byref(d9), p, p, p, p, p, p, p, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd_logits(ctypes.byref(d), p, p, p, p, p, p, p, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_router_bwd(ctypes.byref(d), p, p, None, p, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_bwd(ctypes.byref(d), p, p, p, ctypes.c_void_p(4), None) == _lib.MOE_ERR_INVALID_ARG
