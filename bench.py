@@ -295,6 +295,40 @@ def router_record(wl, dev, warmup, iters, seed=0):
             "algorithmic_mb": round(nbytes / 1e6, 3), "router_gbps": round(nbytes / (t_router * 1e-6) / 1e9, 1)}
 
 
+def separate_record(runner, warmup, iters):
+    """The fwd (Z saved) + bwd step with the gate and up weights as two
+    [E,I,H] tensors (moe_fwd_sep / moe_bwd_sep), beside the same step with
+    the fused [E,2I,H] tensor, each iteration after the cache flush."""
+    import numpy as np
+    import torch
+    import mixture_experts_expert_histogram_amd as moe
+    wl = runner.wl
+    I = wl.I
+    W = runner.Wgu
+    wg, wu = ((W[:, 0::2], W[:, 1::2]) if wl.layout == "interleaved" else (W[:, :I], W[:, I:]))
+    wg, wu = wg.contiguous(), wu.contiguous()
+    gdt = runner.grads[2].dtype
+    sep_grads = (runner.grads[0], runner.grads[1], torch.empty_like(wg, dtype=gdt), torch.empty_like(wu, dtype=gdt),
+                 runner.grads[3])
+    kw = dict(act=wl.act, limit=wl.limit, alpha=wl.alpha)
+
+    def step_sep():
+        moe.fwd_sep(runner.X, runner.ids, runner.w, wg, wu, runner.Wd, save=True, ws=runner.ws_f, out=runner.out,
+                    saved=runner.saved, **kw)
+        moe.bwd_sep(runner.X, runner.ids, runner.w, wg, wu, runner.Wd, runner.dY, saved=runner.saved,
+                    ws=runner.ws_b, grads=sep_grads, grad_dtype=runner.grad_dtype, **kw)
+
+    def step_fused():
+        runner.fwd(True)
+        runner.bwd(True)
+
+    t_sep = float(np.median(runner.time(step_sep, warmup, iters)))
+    t_fused = float(np.median(runner.time(step_fused, warmup, iters)))
+    flops = 18.0 * wl.S * wl.H * wl.I
+    return {"workload": wl.name, "pass": "fwd+bwd", "mode": "separate gate/up weights", "median_ms": round(t_sep, 4),
+            "tflops": round(flops / (t_sep * 1e-3) / 1e12, 2), "fused_median_ms": round(t_fused, 4)}
+
+
 def run_protocol(args):
     import torch
     from synth import WORKLOADS
@@ -302,6 +336,8 @@ def run_protocol(args):
     torch.cuda.set_device(dev)
     for name in ("gptoss", "large", "backward", "zipf"):
         print(json.dumps(router_record(WORKLOADS[name], dev, args.warmup, args.iters)), flush=True)
+    runner = PassRunner(WORKLOADS["gptoss"], dev, grad_dtype=args.grad_dtype)
+    print(json.dumps(separate_record(runner, args.warmup, args.iters)), flush=True)
     current, runner = None, None
     for name, pass_, saved in PROTOCOL:
         if name != current:

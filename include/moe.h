@@ -183,6 +183,29 @@ moe_status_t moe_router_bwd(const moe_desc_t* desc, const int32_t* topk_ids,
                             const float* d_topk_weights, float* d_logits,
                             hipStream_t stream);
 
+/* Separate gate and up weights ("MoE expert parallel execution backward",
+ * description, differentiates gate, up and down weights as three tensors):
+ * w_gate, w_up [E,I,H] in place of w_gate_up, and in moe_bwd_sep d_w_gate,
+ * d_w_up [E,I,H] (grad_dtype) in place of d_w_gate_up; gate and up rows are
+ * then g = w_gate[e].x and u = w_up[e].x, and desc->gu_layout is ignored.
+ * Everything else (outputs, workspace sizes, `saved`, errors) is as for
+ * moe_fwd / moe_bwd; a `saved` buffer filled by moe_fwd_sep is meant for
+ * moe_bwd_sep (its Z columns are the I gate columns, then the I up columns).
+ * w_up and d_w_up must not be NULL. */
+moe_status_t moe_fwd_sep(const moe_desc_t* desc, const void* hidden,
+                         const int32_t* topk_ids, const float* topk_weights,
+                         const void* w_gate, const void* w_up,
+                         const void* w_down, void* out, void* saved, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+moe_status_t moe_bwd_sep(const moe_desc_t* desc, const void* hidden,
+                         const int32_t* topk_ids, const float* topk_weights,
+                         const void* w_gate, const void* w_up,
+                         const void* w_down, const void* d_out,
+                         const void* saved, void* d_hidden,
+                         float* d_topk_weights, void* d_w_gate, void* d_w_up,
+                         void* d_w_down, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* Synchronises `stream` and reports MOE_ERR_BAD_EXPERT_ID if the last
  * routing done in `ws` met an id outside [0,E), else MOE_OK. */
 moe_status_t moe_check_device_status(const void* ws, hipStream_t stream);

@@ -5,7 +5,8 @@ The computation runs in hand-written HIP kernels behind the C ABI declared in
 the library in-tree.
 """
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, MoeDesc, MoeError, bwd, check_device_status, empty_workspace, fwd, fwd_logits, library,
+    EXPORTED, LIB_PATH, MoeDesc, MoeError, bwd, bwd_sep, check_device_status, empty_workspace, fwd, fwd_logits,
+    fwd_sep, library,
     make_desc, route, route_workspace_size, router, router_bwd, status_str, timing_disable, timing_enable,
     timing_read, workspace_size,
 )

@@ -19,8 +19,8 @@ MOE_SWIGLU, MOE_CLAMPED_GLU = 0, 1
 MOE_GU_CONCAT, MOE_GU_INTERLEAVED = 0, 1
 
 EXPORTED = ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_router", "moe_fwd",
-            "moe_fwd_logits", "moe_bwd", "moe_router_bwd", "moe_check_device_status", "moe_status_str",
-            "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]
+            "moe_fwd_logits", "moe_fwd_sep", "moe_bwd", "moe_bwd_sep", "moe_router_bwd", "moe_check_device_status",
+            "moe_status_str", "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]
 
 
 class MoeDesc(ctypes.Structure):
@@ -63,6 +63,8 @@ def library() -> ctypes.CDLL:
     lib.moe_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_fwd_logits.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_router_bwd.argtypes = [pd, vp, vp, vp, vp, vp]
+    lib.moe_fwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_bwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_check_device_status.argtypes = [vp, vp]
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -71,8 +73,8 @@ def library() -> ctypes.CDLL:
     lib.moe_timing_disable.argtypes = []
     lib.moe_timing_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     for name in ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_router", "moe_fwd",
-                 "moe_fwd_logits", "moe_bwd", "moe_router_bwd", "moe_check_device_status", "moe_timing_enable",
-                 "moe_timing_disable", "moe_timing_read"]:
+                 "moe_fwd_logits", "moe_fwd_sep", "moe_bwd", "moe_bwd_sep", "moe_router_bwd",
+                 "moe_check_device_status", "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -272,6 +274,61 @@ def bwd(hidden, topk_ids, topk_weights, w_gate_up, w_down, d_out, saved=None, ac
                              _ptr(d_out.contiguous()), _ptr(saved), _ptr(dh), _ptr(dw), _ptr(dgu), _ptr(dd),
                              _ptr(ws), ws.numel(), _stream()), "moe_bwd")
     return dh, dw, dgu, dd, ws
+
+
+def _sep_desc(hidden, topk_ids, w_gate, w_up, w_down, act, limit, alpha, grad_dtype=None) -> MoeDesc:
+    import torch
+    T, H = hidden.shape
+    E, I, H2 = w_gate.shape
+    if (H2 != H or tuple(w_up.shape) != (E, I, H) or tuple(w_down.shape) != (E, H, I)
+            or topk_ids.shape[0] != T):
+        raise ValueError("inconsistent MoE shapes")
+    for t in (hidden, w_gate, w_up, w_down):
+        if t.dtype != hidden.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("hidden and weights must be contiguous device tensors of one dtype")
+    dt = "bf16" if hidden.dtype == torch.bfloat16 else ("fp32" if hidden.dtype == torch.float32 else None)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {hidden.dtype}")
+    return make_desc(T, H, I, E, topk_ids.shape[1], dt, act, "concat", limit, alpha, grad_dtype)
+
+
+def fwd_sep(hidden, topk_ids, topk_weights, w_gate, w_up, w_down, act="swiglu", limit=7.0, alpha=1.702, save=False,
+            ws=None, out=None, saved=None):
+    """Forward with separate gate and up weights [E, I, H]; returns (out, saved-or-None, ws)."""
+    import torch
+    d = _sep_desc(hidden, topk_ids, w_gate, w_up, w_down, act, limit, alpha)
+    ids, w = _ids32(topk_ids), _f32(topk_weights)
+    fws, _, sbytes = workspace_size(d)
+    ws = empty_workspace(fws, hidden.device) if ws is None else ws
+    out = torch.empty_like(hidden) if out is None else out
+    if save and saved is None:
+        saved = empty_workspace(sbytes, hidden.device)
+    _check(library().moe_fwd_sep(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate), _ptr(w_up),
+                                 _ptr(w_down), _ptr(out), _ptr(saved) if save else None, _ptr(ws), ws.numel(),
+                                 _stream()), "moe_fwd_sep")
+    return out, (saved if save else None), ws
+
+
+def bwd_sep(hidden, topk_ids, topk_weights, w_gate, w_up, w_down, d_out, saved=None, act="swiglu", limit=7.0,
+            alpha=1.702, ws=None, grads=None, grad_dtype=None):
+    """Backward with separate gate and up weights; returns
+    (d_hidden, d_topk_weights, d_w_gate, d_w_up, d_w_down, ws)."""
+    import torch
+    d = _sep_desc(hidden, topk_ids, w_gate, w_up, w_down, act, limit, alpha, grad_dtype)
+    ids, w = _ids32(topk_ids), _f32(topk_weights)
+    _, bws, _ = workspace_size(d)
+    ws = empty_workspace(bws, hidden.device) if ws is None else ws
+    if grads is None:
+        gdt = torch.float32 if d.grad_dtype == MOE_F32 else torch.bfloat16
+        grads = (torch.empty_like(hidden), torch.empty(ids.shape, dtype=torch.float32, device=hidden.device),
+                 torch.empty(w_gate.shape, dtype=gdt, device=hidden.device),
+                 torch.empty(w_up.shape, dtype=gdt, device=hidden.device),
+                 torch.empty(w_down.shape, dtype=gdt, device=hidden.device))
+    dh, dw, dg, du, dd = grads
+    _check(library().moe_bwd_sep(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate), _ptr(w_up),
+                                 _ptr(w_down), _ptr(d_out.contiguous()), _ptr(saved), _ptr(dh), _ptr(dw), _ptr(dg),
+                                 _ptr(du), _ptr(dd), _ptr(ws), ws.numel(), _stream()), "moe_bwd_sep")
+    return dh, dw, dg, du, dd, ws
 
 
 def check_device_status(ws) -> int:

@@ -29,7 +29,7 @@ struct Layout {
   size_t status, counts, offsets, tile_prefix, expert_order, blk_hist, blk_bad;
   size_t sorted_slot, inv_pos, tok_of_pos, w_of_pos, route_end;
   // forward
-  size_t f_xp, f_a, f_y, f_end;
+  size_t f_a, f_y, f_end;
   // backward
   size_t b_xp, b_dyp, b_z, b_dz, b_aw, b_part, b_dx, b_end;
 };
@@ -52,7 +52,6 @@ Layout make_layout(const Dims& d) {
   L.route_end = o;
   // hidden / d_out rows gathered into expert order
   const size_t perm_rows = (size_t)d.S * d.H * d.esz;
-  L.f_xp = take(0);
   L.f_a = take((size_t)d.S * d.I * d.esz);
   L.f_y = take((size_t)d.S * d.H * sizeof(float));
   L.f_end = o;
@@ -87,10 +86,6 @@ RouteState route_state(void* ws, const Layout& L, const Dims& d) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// The LDS-DMA bf16 engine (gemm_bf16.hip) is off until its GPU fault is
-// understood; bf16 then runs on the register-staged engine (gemm.hip).
-bool lds_dma_engine_enabled() { return false; }
 
 // Shape and enum checks shared by every entry point.
 moe_status_t check_desc(const moe_desc_t* desc, Dims* d) {
@@ -272,14 +267,23 @@ moe_status_t moe_router_bwd(const moe_desc_t* desc, const int32_t* topk_ids, con
 
 static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                              const float* topk_weights, const float* logits, int32_t* ids_out, float* w_out,
-                             const void* w_gate_up, const void* w_down, void* out, void* saved, void* ws,
-                             size_t ws_bytes, hipStream_t stream);
+                             const void* w_gate_up, const void* w_up, const void* w_down, void* out, void* saved,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                      const float* topk_weights, const void* w_gate_up, const void* w_down, void* out, void* saved,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
   if (desc && desc->T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
-  return fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate_up, w_down, out, saved,
+  return fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate_up, nullptr, w_down, out,
+                  saved, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_fwd_sep(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                         const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
+                         void* out, void* saved, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (desc && desc->T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  if (!w_up) return MOE_ERR_INVALID_ARG;
+  return fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate, w_up, w_down, out, saved,
                   ws, ws_bytes, stream);
 }
 
@@ -288,22 +292,23 @@ moe_status_t moe_fwd_logits(const moe_desc_t* desc, const void* hidden, const fl
                             float* topk_weights, void* saved, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (desc && desc->T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
   if (desc && desc->K > desc->E) return MOE_ERR_INVALID_ARG;
-  return fwd_impl(desc, hidden, topk_ids, topk_weights, logits, topk_ids, topk_weights, w_gate_up, w_down, out,
-                  saved, ws, ws_bytes, stream);
+  return fwd_impl(desc, hidden, topk_ids, topk_weights, logits, topk_ids, topk_weights, w_gate_up, nullptr, w_down,
+                  out, saved, ws, ws_bytes, stream);
 }
 
 // Forward from given ids and weights (logits == NULL) or from router logits
-// (ids_out / w_out receive the router's choice).
+// (ids_out / w_out receive the router's choice); w_up != NULL: w_gate_up is
+// the gate tensor [E,I,H] and w_up the up tensor.
 static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                              const float* topk_weights, const float* logits, int32_t* ids_out, float* w_out,
-                             const void* w_gate_up, const void* w_down, void* out, void* saved, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+                             const void* w_gate_up, const void* w_up, const void* w_down, void* out, void* saved,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
   Dims d;
   moe_status_t st = check_desc(desc, &d);
   if (st != MOE_OK) return st;
   if (!w_gate_up || !w_down || !ws) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!hidden || !topk_ids || !topk_weights || !out)) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {hidden, topk_ids, topk_weights, logits, w_gate_up, w_down, out, saved, ws};
+  const void* ptrs[] = {hidden, topk_ids, topk_weights, logits, w_gate_up, w_up, w_down, out, saved, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
@@ -314,6 +319,10 @@ static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const i
   }
   RouteState rs = route_state(ws, L, d);
   GemmProblem pb = problem(desc, d, &rs);
+  if (w_up) {
+    pb.w_up = w_up;
+    pb.layout = 0;   // Z columns: gate then up
+  }
   char* b = (char*)ws;
   void* a = b + L.f_a;
   float* yp = (float*)(b + L.f_y);
@@ -321,43 +330,49 @@ static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const i
     HIP_TRY(launch_route_logits(logits, (int)d.T, (int)d.K, (int)d.E, ids_out, w_out, rs, stream));
   else
     HIP_TRY(launch_route(topk_ids, topk_weights, (int)d.S, (int)d.K, (int)d.E, rs, stream));
-  if (pb.dtype == 0 && lds_dma_engine_enabled()) {
-    void* xp = b + L.f_xp;
-    HIP_TRY(launch_gather_rows(hidden, rs.tok_of_pos, (int)d.S, d.H * d.esz, xp, stream));
-    HIP_TRY(launch_gate_up_bf16(pb, xp, w_gate_up, a, saved, stream));
-    HIP_TRY(launch_down_bf16(pb, a, w_down, yp, stream));
-  } else {
-    HIP_TRY(launch_gate_up(pb, hidden, w_gate_up, a, saved, stream));
-    HIP_TRY(launch_down(pb, a, w_down, yp, stream));
-  }
+  HIP_TRY(launch_gate_up(pb, hidden, w_gate_up, a, saved, stream));
+  HIP_TRY(launch_down(pb, a, w_down, yp, stream));
   HIP_TRY(launch_combine(pb.dtype, yp, rs.inv_pos, (int)d.T, (int)d.K, (int)d.H, out, stream));
   return MOE_OK;
 }
 
-moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
-                     const float* topk_weights, const void* w_gate_up, const void* w_down, const void* d_out,
-                     const void* saved, void* d_hidden, float* d_topk_weights, void* d_w_gate_up, void* d_w_down,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
+// Backward; w_up != NULL: w_gate_up / d_w_gate_up are the gate tensors
+// [E,I,H] and w_up / d_w_up the up tensors.
+static moe_status_t bwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, const void* w_gate_up, const void* w_up, const void* w_down,
+                             const void* d_out, const void* saved, void* d_hidden, float* d_topk_weights,
+                             void* d_w_gate_up, void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   Dims d;
   moe_status_t st = check_desc(desc, &d);
   if (st != MOE_OK) return st;
   if (!w_gate_up || !w_down || !d_w_gate_up || !d_w_down || !ws) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!hidden || !topk_ids || !topk_weights || !d_out || !d_hidden || !d_topk_weights))
     return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {hidden, topk_ids, topk_weights, w_gate_up, w_down, d_out, saved,
-                        d_hidden, d_topk_weights, d_w_gate_up, d_w_down, ws};
+  const void* ptrs[] = {hidden, topk_ids, topk_weights, w_gate_up, w_up, w_down, d_out, saved,
+                        d_hidden, d_topk_weights, d_w_gate_up, d_w_up, d_w_down, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
   if (ws_bytes < L.b_end) return MOE_ERR_WORKSPACE;
   if (d.T == 0) {   // no slots: zero weight gradients, and a status word that reports this call
     HIP_TRY(launch_fill_zero((char*)ws + L.status, 4 * sizeof(int32_t), stream));
-    HIP_TRY(launch_fill_zero(d_w_gate_up, (size_t)d.E * 2 * d.I * d.H * d.gsz, stream));
+    if (w_up) {
+      HIP_TRY(launch_fill_zero(d_w_gate_up, (size_t)d.E * d.I * d.H * d.gsz, stream));
+      HIP_TRY(launch_fill_zero(d_w_up, (size_t)d.E * d.I * d.H * d.gsz, stream));
+    } else {
+      HIP_TRY(launch_fill_zero(d_w_gate_up, (size_t)d.E * 2 * d.I * d.H * d.gsz, stream));
+    }
     HIP_TRY(launch_fill_zero(d_w_down, (size_t)d.E * d.H * d.I * d.gsz, stream));
     return MOE_OK;
   }
   RouteState rs = route_state(ws, L, d);
   GemmProblem pb = problem(desc, d, &rs);
+  if (w_up) {
+    pb.w_up = w_up;
+    pb.dw_up = d_w_up;
+    pb.layout = 0;   // Z and dZ columns: gate then up
+  }
   char* b = (char*)ws;
   void* z = b + L.b_z;
   void* dz = b + L.b_dz;
@@ -367,23 +382,6 @@ moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* 
   HIP_TRY(launch_route(topk_ids, topk_weights, (int)d.S, (int)d.K, (int)d.E, rs, stream));
   const void* zsrc = saved;
   int nparts = 0;
-  if (pb.dtype == 0 && lds_dma_engine_enabled()) {
-    void* xp = b + L.b_xp;
-    void* dyp = b + L.b_dyp;
-    HIP_TRY(launch_gather_rows(hidden, rs.tok_of_pos, (int)d.S, d.H * d.esz, xp, stream));
-    HIP_TRY(launch_gather_rows(d_out, rs.tok_of_pos, (int)d.S, d.H * d.esz, dyp, stream));
-    if (!zsrc) {
-      HIP_TRY(launch_gate_up_bf16(pb, xp, w_gate_up, nullptr, z, stream));
-      zsrc = z;
-    }
-    HIP_TRY(launch_down_dgrad_bf16(pb, dyp, w_down, (const float*)zsrc, dz, aw, part, &nparts, stream));
-    HIP_TRY(launch_topkw_reduce(part, nparts, rs.inv_pos, (int)d.S, d_topk_weights, stream));
-    HIP_TRY(launch_gate_up_dgrad_bf16(pb, dz, w_gate_up, dx, stream));
-    HIP_TRY(launch_combine(pb.dtype, dx, rs.inv_pos, (int)d.T, (int)d.K, (int)d.H, d_hidden, stream));
-    HIP_TRY(launch_wgrad_down_bf16(pb, dyp, aw, d_w_down, stream));
-    HIP_TRY(launch_wgrad_gate_up_bf16(pb, dz, xp, d_w_gate_up, stream));
-    return MOE_OK;
-  }
   void* xp = b + L.b_xp;
   void* dyp = b + L.b_dyp;
   HIP_TRY(launch_gather_rows(hidden, rs.tok_of_pos, (int)d.S, d.H * d.esz, xp, stream));
@@ -399,6 +397,24 @@ moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* 
   HIP_TRY(launch_wgrad_down(pb, dyp, aw, d_w_down, stream));
   HIP_TRY(launch_wgrad_gate_up(pb, dz, xp, d_w_gate_up, stream));
   return MOE_OK;
+}
+
+moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                     const float* topk_weights, const void* w_gate_up, const void* w_down, const void* d_out,
+                     const void* saved, void* d_hidden, float* d_topk_weights, void* d_w_gate_up, void* d_w_down,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate_up, nullptr, w_down, d_out, saved, d_hidden,
+                  d_topk_weights, d_w_gate_up, nullptr, d_w_down, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_bwd_sep(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                         const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
+                         const void* d_out, const void* saved, void* d_hidden, float* d_topk_weights,
+                         void* d_w_gate, void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!w_up || !d_w_up) return MOE_ERR_INVALID_ARG;
+  return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate, w_up, w_down, d_out, saved, d_hidden,
+                  d_topk_weights, d_w_gate, d_w_up, d_w_down, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_check_device_status(const void* ws, hipStream_t stream) {

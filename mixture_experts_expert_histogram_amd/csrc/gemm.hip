@@ -570,7 +570,30 @@ struct GArgs {
   float limit, alpha;
   int ntn, ntm, nparts;
   int big;   // weight grads: experts with more positions than this are split over the XCDs
+  // Gate/up rows of the weights (gu_*) and of their gradients (dgu_*): row j of
+  // expert e's gate (up) projection starts gu_es*e + gu_rs*j elements after
+  // gu_g (gu_u).  Fused [E,2I,H] concatenated: (W, W + I*H, 2IH, H);
+  // interleaved: (W, W + H, 2IH, 2H); separate [E,I,H] tensors: (Wg, Wu, IH, H).
+  const void* gu_g;
+  const void* gu_u;
+  void* dgu_g;
+  void* dgu_u;
+  long gu_es, gu_rs;
+  int gu_sep;   // separate gate and up tensors (Z and dZ columns then concatenated)
 };
+
+// Row j of expert e's gate (up = 0) or up (up = 1) projection.
+template <typename P>
+__device__ __forceinline__ P* gu_row(P* g0, P* u0, long es, long rs, int e, int up, int j) {
+  return (up ? u0 : g0) + es * e + rs * j;
+}
+
+// Gate/up half and index of column m of Z and dZ [S,2I] (interleaved:
+// columns 2j, 2j+1; otherwise gate columns [0,I), up columns [I,2I)).
+__device__ __forceinline__ void zcol(int m, int I, int layout, int& up, int& j) {
+  up = layout ? (m & 1) : (m >= I);
+  j = layout ? (m >> 1) : m - (up ? I : 0);
+}
 
 // Token-row tiles: (expert, N-tile, M-tile of BM rows), ordered by expert,
 // then N-tile, then M-tile, so the M-tiles of one expert that share a weight
@@ -651,7 +674,6 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_kernel(GArgs g) {
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
   const int H = g.H, I = g.I;
   const T* X = (const T*)g.A;
-  const T* W = (const T*)g.B + (size_t)e * 2 * I * H;
   const int j0 = nt * (C::BN / 2);
   const int layout = g.layout;
   const int* tok = g.tok_of_pos;
@@ -661,10 +683,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_kernel(GArgs g) {
   al.init([&](int r) { return X + (size_t)tok[m0 + min(r, rows - 1)] * H; }, H);
   bl.init([&](int r) {
     const int q = r >> 5;
-    int j = j0 + ((q >> 1) << 5) + (r & 31);
-    j = min(j, I - 1);
-    const int wrow = layout ? (2 * j + (q & 1)) : ((q & 1) ? I + j : j);
-    return W + (size_t)wrow * H;
+    const int j = min(j0 + ((q >> 1) << 5) + (r & 31), I - 1);
+    return gu_row((const T*)g.gu_g, (const T*)g.gu_u, g.gu_es, g.gu_rs, e, q & 1, j);
   }, H);
   f32x16 acc[C::FM][C::FN];
   mainloop_rows<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
@@ -828,15 +848,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void down_dgrad_kernel(GArgs g) {
 }
 
 // ---------------------------------------------------------------- gate_up dgrad
-// dXp[p, h] = sum_j dZ[p, j] * Wgu[e][j, h]
-template <class C>
+// dXp[p, h] = sum over the 2I columns m of dZ[p, m] * (gate or up row of m)[h]
+template <class C, bool SEP>
 __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
   int e, m0, rows, nt;
   if (!row_tile<C::BM>(g, e, m0, rows, nt)) return;
-  const int H = g.H, I2 = 2 * g.I;
+  const int H = g.H, I = g.I, I2 = 2 * g.I;
   const T* dZ = (const T*)g.A;
-  const T* W = (const T*)g.B + (size_t)e * I2 * H;
   const int n0 = nt * C::BN;
   RowLoader<C, C::BM, 0> al;
   MNLoader<C, C::NT / 2> bl;
@@ -844,8 +863,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
   bl.init(H - n0, I2);
   f32x16 acc[C::FM][C::FN];
   auto aload = [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); };
+  // Row k of the weights in dZ-column order: in both fused layouts the fused
+  // rows are in that order already (bg + k*H); separate tensors (SEP) switch
+  // to the up tensor at k = I.
+  const T* bg = (const T*)g.gu_g + g.gu_es * e + n0;
+  const T* bu = (const T*)g.gu_u + g.gu_es * e + n0;
   auto bload = [&](auto& l, int kt, auto set) {
-    l.template load<decltype(set)::value>(kt, [&](int k) { return W + (size_t)k * H + n0; });
+    l.template load<decltype(set)::value>(kt, [&](int k) {
+      if constexpr (SEP) return k >= I ? bu + (size_t)(k - I) * H : bg + (size_t)k * H;
+      else return bg + (size_t)k * H;
+    });
   };
   const int nk = (I2 + C::BK - 1) / C::BK;
   if constexpr (kTwoSets<C>) mainloop<C, false, true>(al, bl, aload, bload, nk, lds, acc);
@@ -1057,7 +1084,7 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
     uint4 v[PER];
     OutT* dWt = dW;        // tile origin in dW of the registers' tile
     int next_q = NQ;       // next quarter to write (NQ: none pending)
-    int stage_rows = 0, stage_cols = 0;
+    int stage_rows = 0, stage_cols = 0, stage_e = 0, stage_m0 = 0, stage_n0 = 0;
     auto write_quarter = [&](int q) {
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) {
@@ -1067,7 +1094,15 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
           const int i = qq * QS + j;
           const int idx = tid + i * kStoreThreads;
           const int r = idx / ST::CPR, c = (idx % ST::CPR) * VPC;
-          if (r < stage_rows && c < stage_cols) *(uint4*)(dWt + (size_t)r * N + c) = v[i];
+          if (r < stage_rows && c < stage_cols) {
+            OutT* row = dWt + (size_t)r * N;   // fused dW: tile rows are consecutive rows
+            if (GATE_UP && g.gu_sep) {           // separate dW_gate, dW_up: row m0 + r is a dZ column
+              int up, j;
+              zcol(stage_m0 + r, I, g.layout, up, j);
+              row = gu_row((OutT*)g.dgu_g, (OutT*)g.dgu_u, g.gu_es, g.gu_rs, stage_e, up, j) + stage_n0;
+            }
+            *(uint4*)(row + c) = v[i];
+          }
         }
       }
     };
@@ -1084,6 +1119,9 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
           v[i] = ST::read(stage, idx / ST::CPR, idx % ST::CPR);
         }
         dWt = dW + ((size_t)cur.e * M + cur.m0) * N + cur.n0;
+        stage_e = cur.e;
+        stage_m0 = cur.m0;
+        stage_n0 = cur.n0;
         stage_rows = min(C::BM, M - cur.m0);
         stage_cols = min(C::BN, N - cur.n0);
         next_q = 0;
@@ -1211,6 +1249,29 @@ static GArgs base_args(const GemmProblem& pb, int bm) {
   return g;
 }
 
+// The gate/up row view of a weight-shaped tensor (see GArgs).
+static void gu_view(const GemmProblem& pb, const void* fused_or_gate, const void* up, size_t esz, const void*& g0,
+                    const void*& u0) {
+  const size_t IH = (size_t)pb.I * pb.H;
+  g0 = fused_or_gate;
+  if (pb.w_up) u0 = up;
+  else u0 = (const char*)fused_or_gate + (pb.layout ? (size_t)pb.H : IH) * esz;
+}
+static void set_gu(GArgs& g, const GemmProblem& pb, const void* w, void* dw, size_t dw_esz) {
+  const size_t esz = pb.dtype == 0 ? 2 : 4;
+  const long IH = (long)pb.I * pb.H;
+  g.gu_sep = pb.w_up != nullptr;
+  g.gu_es = pb.w_up ? IH : 2 * IH;
+  g.gu_rs = (!pb.w_up && pb.layout) ? 2L * pb.H : pb.H;
+  if (w) gu_view(pb, w, pb.w_up, esz, g.gu_g, g.gu_u);
+  if (dw) {
+    const void *dg, *du;
+    gu_view(pb, dw, pb.dw_up, dw_esz, dg, du);
+    g.dgu_g = (void*)dg;
+    g.dgu_u = (void*)du;
+  }
+}
+
 static int mtiles_upper(int S, int E, int bm) { return (S + bm - 1) / bm + (E < S ? E : S); }
 // Token-row grids: worst-case tile count, rounded up to 8 plus 8 (see row_tile).
 static long row_grid(const GemmProblem& pb, int bm, int ntn) {
@@ -1223,6 +1284,7 @@ static hipError_t gate_up_impl(const GemmProblem& pb, const void* X, const void*
                                hipStream_t s) {
   GArgs g = base_args(pb, C::BM);
   g.A = X; g.B = Wgu; g.out0 = a_out; g.out1 = z_out;
+  set_gu(g, pb, Wgu, nullptr, 0);
   g.ntn = (pb.I + C::BN / 2 - 1) / (C::BN / 2);
   const long grid = row_grid(pb, C::BM, g.ntn);
   return run_kernel(A ? "gate_up_glu" : "gate_up_z", s, [&] { gate_up_kernel<C, A, Z><<<grid, C::NT, 0, s>>>(g); });
@@ -1287,9 +1349,13 @@ static hipError_t gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, cons
                                      hipStream_t s) {
   GArgs g = base_args(pb, C::BM);
   g.A = dZ; g.B = Wgu; g.out0 = dXp;
+  set_gu(g, pb, Wgu, nullptr, 0);
   g.ntn = (pb.H + C::BN - 1) / C::BN;
   const long grid = row_grid(pb, C::BM, g.ntn);
-  return run_kernel("gate_up_dgrad", s, [&] { gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+  return run_kernel("gate_up_dgrad", s, [&] {
+    if (g.gu_sep) gate_up_dgrad_kernel<C, true><<<grid, C::NT, 0, s>>>(g);
+    else gate_up_dgrad_kernel<C, false><<<grid, C::NT, 0, s>>>(g);
+  });
 }
 
 hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
@@ -1310,9 +1376,16 @@ static int device_cus() {
 template <class C, bool GU, typename OutT>
 static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
   const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
-  if (pb.S == 0) return launch_fill_zero(dW, (size_t)pb.E * M * N * sizeof(OutT), s);   // no positions
+  if (pb.S == 0) {   // no positions
+    if (GU && pb.dw_up) {
+      const hipError_t e = launch_fill_zero(dW, (size_t)pb.E * pb.I * N * sizeof(OutT), s);
+      return e != hipSuccess ? e : launch_fill_zero(pb.dw_up, (size_t)pb.E * pb.I * N * sizeof(OutT), s);
+    }
+    return launch_fill_zero(dW, (size_t)pb.E * M * N * sizeof(OutT), s);
+  }
   GArgs g = base_args(pb, C::BM);
   g.A = A; g.B = B; g.out0 = dW;
+  if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
   g.ntm = (M + C::BM - 1) / C::BM;
   g.ntn = (N + C::BN - 1) / C::BN;
   // split experts: more than twice the mean positions per expert (and more than 4 k-steps)

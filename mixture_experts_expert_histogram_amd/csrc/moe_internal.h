@@ -68,6 +68,11 @@ struct GemmProblem {
   float limit, alpha;
   int T, H, I, E, K, S;
   const RouteState* rs;
+  // separate gate and up weights: the launches' w_gate_up / d_w_gate_up
+  // arguments are then the gate tensors [E,I,H] and these the up tensors
+  // (layout is then the concatenated one for Z and dZ); null when fused
+  const void* w_up = nullptr;
+  void* dw_up = nullptr;
 };
 // Per-slot buffers are indexed by the expert-sorted position p.
 // forward gate_up projection + GLU: writes a [S,I] (dtype, if a_out) and Z fp32 [S,2I] (if z_out)
@@ -89,18 +94,6 @@ hipError_t launch_wgrad_down(const GemmProblem& pb, const void* dY, const void* 
 hipError_t launch_wgrad_gate_up(const GemmProblem& pb, const void* dZ, const void* X, void* dWgu,
                                 hipStream_t stream);
 
-// ---- bf16 engine (gemm_bf16.hip): operands are pre-gathered into expert order
-hipError_t launch_gate_up_bf16(const GemmProblem& pb, const void* Xp, const void* Wgu, void* a_out, void* z_out,
-                               hipStream_t stream);
-hipError_t launch_down_bf16(const GemmProblem& pb, const void* a, const void* Wd, float* Yp, hipStream_t stream);
-hipError_t launch_down_dgrad_bf16(const GemmProblem& pb, const void* dYp, const void* Wd, const float* Z, void* dZ,
-                                  void* aw, float* partials, int* nparts, hipStream_t stream);
-hipError_t launch_gate_up_dgrad_bf16(const GemmProblem& pb, const void* dZ, const void* Wgu, float* dXp,
-                                     hipStream_t stream);
-hipError_t launch_wgrad_down_bf16(const GemmProblem& pb, const void* dYp, const void* aw, void* dWd,
-                                  hipStream_t stream);
-hipError_t launch_wgrad_gate_up_bf16(const GemmProblem& pb, const void* dZ, const void* Xp, void* dWgu,
-                                     hipStream_t stream);
 // rows dst[p] = src[tok_of_pos[p]] of width `row_bytes` (a multiple of 16)
 hipError_t launch_gather_rows(const void* src, const int32_t* tok_of_pos, int S, size_t row_bytes, void* dst,
                               hipStream_t stream);

@@ -111,3 +111,16 @@ def test_router_argument_errors():
     assert lib.moe_fwd_logits(ctypes.byref(d), p, p, p, p, p, p, p, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
     assert lib.moe_router_bwd(ctypes.byref(d), p, p, None, p, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_router_bwd(ctypes.byref(d), p, p, p, ctypes.c_void_p(4), None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_separate_weight_argument_errors():
+    lib = moe.library()
+    p = ctypes.c_void_p(16)
+    d = moe.make_desc(64, 8, 8, 8, 2)
+    big = 1 << 30
+    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, None, p, p, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, p, p, p, None, p, p, big,
+                           None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, p, p, p, p, p, p, 10,
+                           None) == _lib.MOE_ERR_WORKSPACE
