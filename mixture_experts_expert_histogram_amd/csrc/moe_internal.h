@@ -8,7 +8,7 @@ namespace moe {
 
 // Routing kernels process the slots in chunks of ROUTE_CHUNK per workgroup.
 constexpr int ROUTE_THREADS = 256;
-constexpr int ROUTE_CHUNK = 2048;
+constexpr int ROUTE_CHUNK = 512;
 constexpr int MAX_E = 1024;
 // M-tile heights for which the routing scan writes a tile prefix table.
 constexpr int N_TILE_BM = 5;              // 32, 64, 128, 256, 192

@@ -66,22 +66,45 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int32
                                                           int32_t* __restrict__ status) {
   __shared__ int sh[1024];
   __shared__ int cnt[MAX_E];
+  __shared__ int part[1024];   // [slice][expert]: per-slice sums, then their bases
+  __shared__ int base[MAX_E];
   const int e = threadIdx.x;
+  // The chunks are cut into `slices` contiguous ranges; thread t sums expert
+  // t % E over range t / E, so all 1024 threads read the histogram at once.
+  const int slices = max(1, min(1024 / E, nblk));
+  const int per = (nblk + slices - 1) / slices;
+  const int te = threadIdx.x % E, ts = threadIdx.x / E;
+  const bool slice_thread = threadIdx.x < slices * E;
+  const int b0 = ts * per, b1 = min(nblk, b0 + per);
+  if (slice_thread) {
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += blk_hist[(size_t)b * E + te];
+    part[threadIdx.x] = sum;
+  }
+  __syncthreads();
   int c = 0;
   if (e < E)
-    for (int b = 0; b < nblk; ++b) c += blk_hist[(size_t)b * E + e];
+    for (int q = 0; q < slices; ++q) {   // exclusive scan of the expert's slice sums
+      const int v = part[q * E + e];
+      part[q * E + e] = c;
+      c += v;
+    }
   const int off = block_exclusive_scan_1024(c, sh);
   if (e < E) {
     counts[e] = c;
     offsets[e] = off;
     cnt[e] = c;
-    int run = off;
-    for (int b = 0; b < nblk; ++b) {
-      const int h = blk_hist[(size_t)b * E + e];
-      blk_hist[(size_t)b * E + e] = run;
+    base[e] = off;
+    if (e == E - 1) offsets[E] = off + c;
+  }
+  __syncthreads();
+  if (slice_thread) {   // per-chunk bases of the expert's slots, chunk by chunk
+    int run = base[te] + part[threadIdx.x];
+    for (int b = b0; b < b1; ++b) {
+      const int h = blk_hist[(size_t)b * E + te];
+      blk_hist[(size_t)b * E + te] = run;
       run += h;
     }
-    if (e == E - 1) offsets[E] = off + c;
   }
   for (int j = 0; j < N_TILE_BM; ++j) {
     const int bm = tile_bm(j);
@@ -179,8 +202,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_scatter_kernel(
 // holds logits lane, lane+64, ...; each of K rounds takes the wave-wide best
 // (value, then lower id) of the logits not yet taken.  The histogram, scan
 // and scatter then run on the ids as for given ids.  (Counting the histogram
-// in this kernel instead ties each 2048-slot chunk's tokens to one
-// workgroup, so a 4096-token batch ran on 8 CUs, ~150 us of dependent
+// in this kernel instead ties each chunk's tokens to one workgroup, so with
+// 2048-slot chunks a 4096-token batch ran on 8 CUs, ~150 us of dependent
 // cross-lane reductions; spread out it is a few microseconds.)  A token whose
 // remaining logits are all NaN gets id -1 in the slots left, which the
 // histogram reports as a bad id.
