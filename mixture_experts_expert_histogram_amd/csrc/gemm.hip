@@ -915,11 +915,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
 // written once) dominates the traffic and the K loops are short (an expert's
 // positions), so the kernel is built around keeping the store stream busy:
 //
-// * One persistent workgroup per CU with two roles.  Waves 0-3 load operands
-//   and run the MFMAs; waves 4-7 only write dW.  At the end of a tile the MMA
-//   waves put the fp32 accumulators into an LDS staging tile and go on with
-//   the next tile; the store waves copy the staging tile to dW in whole
-//   512-byte row segments.  A wave's vmcnt counts its loads and stores in
+// * One persistent workgroup per CU with two roles.  The MMA waves (C::NT
+//   threads: 8 waves of 64x32 for bf16) load operands and run the MFMAs; four
+//   more waves only write dW.  At the end of a tile the MMA waves put the
+//   accumulators, converted to the output type, into an LDS staging tile and
+//   go on with the next tile; the store waves copy the staging tile to dW in
+//   whole row segments (256 bytes bf16, 512 bytes fp32).  A wave's vmcnt counts its loads and stores in
 //   issue order, so a wave that did both would wait for its stores before
 //   using later loads; split over two roles, neither stream waits for the
 //   other.
