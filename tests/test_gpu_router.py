@@ -134,3 +134,18 @@ def test_router_reproduces_the_workload_routing(name):
     np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=W_REL)
     np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_ref.ravel(), minlength=wl.E))
+
+
+def test_router_full_size_batch():
+    """The Zipf batch size (32768 tokens) with the large shapes' 256 experts and
+    top-8: every id, count and position bit-exact, every weight to W_REL, and
+    the router backward's rows summing to zero."""
+    T, E, K = 32768, 256, 8
+    lg = logits_case(T, E, 33)
+    ids, w = check_router(lg, K)
+    g = torch.randn((T, K), device="cuda", generator=torch.Generator(device="cuda").manual_seed(3))
+    d = moe.router_bwd(ids, w, g, E)
+    torch.cuda.synchronize()
+    rows = d.double().sum(dim=1).abs()
+    scale = (w.double() * g.double()).abs().sum(dim=1) + 1e-30
+    assert float((rows / scale).max()) < 1e-5
