@@ -49,6 +49,8 @@ def parse():
                         "one JSON line per case and a mean-latency line per shape")
     p.add_argument("--shapes", default="gptoss,large,backward", help="layer shapes of --sweep")
     p.add_argument("--iters", type=int, default=20, help="timed iterations per case of --protocol / --sweep")
+    p.add_argument("--oracle-seconds", type=float, default=6.0,
+                   help="CPU budget of each workload's oracle sample in --protocol")
     return p.parse_args()
 
 
@@ -181,6 +183,32 @@ def pass_record(wl, counts, pass_, grad_bytes, times_ms):
             "experts_with_slots": int((counts > 0).sum())}
 
 
+def oracle_record(wl, runner, budget_s):
+    """The fp64 oracle (forward + backward) on whole experts of the workload,
+    one after another until `budget_s` seconds of CPU time are spent; the tiny
+    workload instead runs whole, ten times (median)."""
+    import numpy as np
+    import oracle
+    from synth import make_dout, make_hidden, make_host_inputs
+    if wl.name == "tiny":
+        inp = make_host_inputs(wl, 0)
+        ex = oracle.expert_accessor(inp.w_gate_up, inp.w_down)
+        times = []
+        for _ in range(10):
+            t0 = time.perf_counter()
+            oracle.forward(inp.hidden, inp.topk_ids, inp.topk_weights, ex, wl.E, wl.act, wl.layout, wl.limit, wl.alpha)
+            oracle.backward(inp.hidden, inp.topk_ids, inp.topk_weights, inp.dout, ex, wl.E, wl.act, wl.layout,
+                            wl.limit, wl.alpha)
+            times.append(time.perf_counter() - t0)
+        sec = float(np.median(times))
+        return {"workload": wl.name, "pass": "oracle fwd+bwd", "seconds": round(sec, 4),
+                "gflops": round(18.0 * wl.S * wl.H * wl.I / sec / 1e9, 3), "sample": "whole workload, median of 10"}
+    rec = cpu_baseline(wl, runner.ids_np, runner.w_np, make_hidden(wl, 0), make_dout(wl, 0), runner.Wgu, runner.Wd,
+                       budget_s)
+    return {"workload": wl.name, "pass": "oracle fwd+bwd", "seconds": rec["seconds"],
+            "gflops": round(rec["value"] * 1e3, 3), "cores": rec["cores"], "sample": rec["sample"]}
+
+
 class PassRunner:
     """Resident inputs, weights, outputs and workspaces of one workload, and
     the timing of its passes with a 512 MiB write between iterations (larger
@@ -196,6 +224,7 @@ class PassRunner:
         from synth import device_weights, make_dout, make_hidden, make_routing, to_device
         self.moe, self.torch, self.wl, self.grad_dtype = moe, torch, wl, grad_dtype
         ids_np, w_np = make_routing(wl, seed=seed)
+        self.ids_np, self.w_np = ids_np, w_np
         self.counts = np.bincount(ids_np.ravel(), minlength=wl.E)
         self.X = to_device(make_hidden(wl, seed), wl, dev)
         self.dY = to_device(make_dout(wl, seed), wl, dev)
@@ -338,6 +367,7 @@ def run_protocol(args):
         print(json.dumps(router_record(WORKLOADS[name], dev, args.warmup, args.iters)), flush=True)
     runner = PassRunner(WORKLOADS["gptoss"], dev, grad_dtype=args.grad_dtype)
     print(json.dumps(separate_record(runner, args.warmup, args.iters)), flush=True)
+    print(json.dumps(oracle_record(WORKLOADS["tiny"], None, 0)), flush=True)
     current, runner = None, None
     for name, pass_, saved in PROTOCOL:
         if name != current:
@@ -346,6 +376,8 @@ def run_protocol(args):
             print(f"[protocol] {name}: drawing inputs", file=sys.stderr, flush=True)
             runner = PassRunner(WORKLOADS[name], dev, grad_dtype=args.grad_dtype)
             current = name
+            if not args.no_cpu_baseline:
+                print(json.dumps(oracle_record(runner.wl, runner, args.oracle_seconds)), flush=True)
         rec = runner.run_pass(pass_, saved, args.warmup, args.iters)
         wl = runner.wl
         mode = ("Z saved" if saved else "Z not kept") if pass_ == "fwd" else ("saved Z" if saved else "recompute Z")
