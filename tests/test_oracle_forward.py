@@ -150,3 +150,21 @@ def test_tiny_workload_runs_and_matches_dense():
     ref = dense_forward(t64(inp.hidden), inp.topk_ids, t64(inp.topk_weights),
                         t64(inp.w_gate_up), t64(inp.w_down), wl.act, wl.layout).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("act,layout", [("swiglu", "concat"), ("clamped", "interleaved")])
+def test_slot_outputs_weight_into_the_forward_and_the_topk_weight_gradient(act, layout):
+    """slot_outputs y[s] (unweighted expert output of slot s) ties out two
+    ways: out[t] = sum_k w[t,k] y[t*K+k], and, since out is linear in the
+    routing weights, dL/dw[t,k] = <dY[t], y[t*K+k]> from the backward."""
+    rng = np.random.default_rng(41)
+    X, ids, w, Wgu, Wd = rand_problem(rng)
+    T, K = ids.shape
+    E = Wgu.shape[0]
+    ex = oracle.expert_accessor(Wgu, Wd)
+    Y = oracle.slot_outputs(X, ids, ex, E, act, layout)
+    out = oracle.forward(X, ids, w, ex, E, act, layout)
+    np.testing.assert_allclose(out, np.einsum("tk,tkh->th", w, Y.reshape(T, K, -1)), rtol=1e-12, atol=1e-12)
+    dY = rng.standard_normal(out.shape)
+    _, dW, _, _ = oracle.backward(X, ids, w, dY, ex, E, act, layout)
+    np.testing.assert_allclose(dW, np.einsum("th,tkh->tk", dY, Y.reshape(T, K, -1)), rtol=1e-12, atol=1e-12)
