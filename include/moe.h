@@ -29,8 +29,9 @@
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers, row-major, contiguous, 16-byte
  *     aligned.  hidden/out/d_out/d_hidden [T,H]; w_gate_up/d_w_gate_up
- *     [E,2I,H]; w_down/d_w_down [E,H,I]; topk_ids int32 [T,K];
- *     topk_weights/d_topk_weights fp32 [T,K].  Activations, weights and
+ *     [E,2I,H]; w_gate/w_up/d_w_gate/d_w_up [E,I,H]; w_down/d_w_down
+ *     [E,H,I]; topk_ids int32 [T,K]; topk_weights/d_topk_weights fp32 [T,K];
+ *     router logits/d_logits fp32 [T,E].  Activations, weights and
  *     d_hidden have the descriptor's dtype (bf16 or fp32); the weight
  *     gradients have its grad_dtype.
  *   - The caller owns every buffer.  The library never allocates device
@@ -49,9 +50,13 @@
  *     from every sum, a flag is set in the workspace, and
  *     moe_check_device_status reports MOE_ERR_BAD_EXPERT_ID; the outputs of
  *     that call are then unspecified.
- *   - T = 0 is valid: nothing is launched for the activations; moe_fwd and
- *     moe_bwd clear the workspace status word (so moe_check_device_status
- *     reports MOE_OK for the call) and moe_bwd writes zero weight gradients.
+ *   - T = 0 is valid: nothing is launched for the activations; the forward
+ *     and backward entry points and moe_router clear the workspace status
+ *     word (so moe_check_device_status reports MOE_OK for the call), and the
+ *     backward entry points write zero weight gradients.
+ *   - Entry points that take router logits or separate gate/up tensors
+ *     (moe_router, moe_fwd_logits, moe_router_bwd, moe_fwd_sep, moe_bwd_sep)
+ *     follow the same conventions; their own comments give the shapes.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
