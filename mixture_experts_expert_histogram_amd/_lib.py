@@ -184,6 +184,8 @@ def router(logits, K: int, ws=None, out=None):
     offsets [E+1], sorted_slot [S], inv_pos [S], ws)."""
     import torch
     lg = _f32(logits)
+    if not lg.is_cuda or lg.dim() != 2:
+        raise ValueError("router takes device logits [T, E]")
     T, E = lg.shape
     d = make_desc(T, 8, 8, E, K)
     dev = lg.device
@@ -205,6 +207,10 @@ def router_bwd(topk_ids, topk_weights, d_topk_weights, E: int, out=None):
     import torch
     ids, w, g = _ids32(topk_ids), _f32(topk_weights), _f32(d_topk_weights)
     T, K = ids.shape
+    if tuple(w.shape) != (T, K) or tuple(g.shape) != (T, K):
+        raise ValueError("topk_ids, topk_weights and d_topk_weights must all be [T, K]")
+    if not (ids.is_cuda and w.is_cuda and g.is_cuda):
+        raise ValueError("router_bwd takes device tensors")
     d = make_desc(T, 8, 8, E, K)
     out = torch.empty((T, E), dtype=torch.float32, device=ids.device) if out is None else out
     _check(library().moe_router_bwd(ctypes.byref(d), _ptr(ids), _ptr(w), _ptr(g), _ptr(out), _stream()),
