@@ -122,6 +122,8 @@ def router_logits(T: int, E: int, seed: int = 0) -> np.ndarray:
 
 def routing_softmax_topk(T: int, E: int, K: int, seed: int = 0):
     """Top-k ids and renormalised softmax weights from N(0,1) router logits."""
+    if K > E:
+        raise ValueError(f"top-{K} routing needs at least {K} experts (E = {E})")
     logits = router_logits(T, E, seed)
     order = np.argsort(-logits, axis=1, kind="stable")[:, :K]
     chosen = np.take_along_axis(logits, order, axis=1).astype(np.float64)

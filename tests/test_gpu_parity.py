@@ -11,7 +11,7 @@ import torch
 
 import mixture_experts_expert_histogram_amd as moe
 import oracle
-from synth import WORKLOADS, make_host_inputs, make_routing
+from synth import WORKLOADS, HostInputs, Workload, make_all_weights, make_dout, make_hidden, make_host_inputs, make_routing
 from tests._gpu import assert_parity, device_inputs, host, oracle_fwd_bwd, small_inputs
 
 pytestmark = pytest.mark.gpu
@@ -178,3 +178,18 @@ def test_no_tokens_gives_zero_weight_grads(grad_dtype):
     torch.cuda.synchronize()
     assert moe.check_device_status(ws) == 0
     assert bool((dgu == 0).all()) and bool((dd == 0).all())
+
+
+@pytest.mark.parametrize("E,K", [(1, 1), (1, 3), (2, 4)])
+def test_degenerate_expert_counts(E, K):
+    """One expert (every slot lands on it, repeatedly when K > 1) and more
+    slots per token than experts: repeated ids are independent slots."""
+    T, H, I = 150, 136, 72
+    rng = np.random.default_rng(E * 10 + K)
+    wl = Workload("degenerate", T, H, I, E, K, "bf16", "swiglu", "concat")
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    gu, dn = make_all_weights(wl, seed=E + K)
+    inp = HostInputs(wl, make_hidden(wl, E + K), ids, w, make_dout(wl, E + K), gu, dn)
+    run_and_compare(inp, grad_dtype="bf16")

@@ -73,3 +73,9 @@ def test_make_routing(name):
     wl = WORKLOADS[name]
     ids, w = make_routing(wl.with_(T=min(wl.T, 256)))
     assert ids.max() < wl.E and ids.min() >= 0
+
+
+def test_softmax_topk_routing_needs_k_experts():
+    from synth import routing_softmax_topk
+    with pytest.raises(ValueError):
+        routing_softmax_topk(4, 2, 3)
