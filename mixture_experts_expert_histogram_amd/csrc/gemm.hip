@@ -114,6 +114,8 @@ struct Cfg {
   static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * (int)sizeof(T);
   // workgroups per CU the launch bounds ask for: two while both fit in LDS
   static constexpr int OCC = LDS_BYTES > 80 * 1024 ? 1 : 2;
+  // 32-bit registers per thread for one k-step of staged operands
+  static constexpr int STAGE_REGS = (A_ELEMS + B_ELEMS) * (int)sizeof(T) / NT / 4;
   static_assert((CPR & (CPR - 1)) == 0, "chunks per row must be a power of two");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   __device__ static __forceinline__ int lds_off(int row, int chunk) {
@@ -664,10 +666,12 @@ template <class C, int ROT>
 using MNLoader = std::conditional_t<sizeof(typename C::elem) == 2, NLoader<C, ROT>, TransLoader<C, 128, ROT>>;
 template <class C> constexpr bool kNLayout = sizeof(typename C::elem) == 2;
 
-// bf16 operands fit the two-set pipeline in 256 registers up to 128-row
-// tiles; taller tiles and fp32 operands use the one-set loop.
+// bf16 operands fit the two-set pipeline in 256 registers when a wave's
+// tile is at most 64x64 and a k-step stages at most 32 registers per thread
+// (128x128 tiles on 4 waves, 256x128 on 8); 192-row tiles (96 rows per wave)
+// and fp32 operands use the one-set loop.
 template <class C>
-constexpr bool kTwoSets = sizeof(typename C::elem) == 2 && C::BM <= 128;
+constexpr bool kTwoSets = sizeof(typename C::elem) == 2 && C::FM * C::FN <= 4 && C::STAGE_REGS <= 32;
 template <class C, class AL, class BL, class ALoadFn, class BLoadFn>
 __device__ __forceinline__ void mainloop_rows(AL& al, BL& bl, ALoadFn aload, BLoadFn bload, int nk,
                                               typename C::elem* lds, f32x16 (&acc)[C::FM][C::FN]) {
@@ -1243,6 +1247,17 @@ static bool use_bm192(const GemmProblem& pb) {
   const long mean = pb.E > 0 ? (long)pb.S / pb.E : 0;
   return pb.dtype == 0 && mean > 100 && mean <= 176;
 }
+// bf16 with 256x128 tiles on 8 waves (64x64 each, one workgroup per CU):
+// when experts average several hundred positions, a quarter fewer operand
+// bytes per flop from L2 than 128x128 tiles (Zipf workload: gate_up 6.42 ->
+// 6.24 ms, down 3.09 -> 2.97, gate_up_dgrad 6.32 -> 5.96).  The same tile on
+// 4 waves of 128x64 was slower: with one wave per SIMD nothing covers a
+// step's barrier and first LDS reads.
+using CfgB256 = Cfg<uint16_t, 256, 128, 64, 4, 2>;
+static bool use_bm256(const GemmProblem& pb) {
+  const long mean = pb.E > 0 ? (long)pb.S / pb.E : 0;
+  return pb.dtype == 0 && mean >= 320;
+}
 using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
 // weight gradients (one persistent workgroup per CU: operands, staging tile and tables in LDS)
 using CfgWB = Cfg<uint16_t, 128, 128, 64, 2, 4>;
@@ -1316,6 +1331,7 @@ hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu,
                           hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
   if (pb.dtype != 0) return gate_up_dispatch<CfgF>(pb, X, Wgu, a_out, z_out, s);
+  if (use_bm256(pb)) return gate_up_dispatch<CfgB256>(pb, X, Wgu, a_out, z_out, s);
   return use_bm192(pb) ? gate_up_dispatch<CfgB192>(pb, X, Wgu, a_out, z_out, s)
                        : gate_up_dispatch<CfgB>(pb, X, Wgu, a_out, z_out, s);
 }
@@ -1332,6 +1348,7 @@ static hipError_t down_impl(const GemmProblem& pb, const void* a, const void* Wd
 hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
   if (pb.dtype != 0) return down_impl<CfgF>(pb, a, Wd, Yp, s);
+  if (use_bm256(pb)) return down_impl<CfgB256>(pb, a, Wd, Yp, s);
   return use_bm192(pb) ? down_impl<CfgB192>(pb, a, Wd, Yp, s) : down_impl<CfgB>(pb, a, Wd, Yp, s);
 }
 
@@ -1375,6 +1392,7 @@ static hipError_t gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, cons
 hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
   if (pb.dtype != 0) return gate_up_dgrad_impl<CfgF>(pb, dZ, Wgu, dXp, s);
+  if (use_bm256(pb)) return gate_up_dgrad_impl<CfgB256>(pb, dZ, Wgu, dXp, s);
   return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(pb, dZ, Wgu, dXp, s)
                        : gate_up_dgrad_impl<CfgB>(pb, dZ, Wgu, dXp, s);
 }

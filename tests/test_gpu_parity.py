@@ -193,3 +193,13 @@ def test_degenerate_expert_counts(E, K):
     gu, dn = make_all_weights(wl, seed=E + K)
     inp = HostInputs(wl, make_hidden(wl, E + K), ids, w, make_dout(wl, E + K), gu, dn)
     run_and_compare(inp, grad_dtype="bf16")
+
+
+@pytest.mark.parametrize("act,layout", [("swiglu", "concat"), ("clamped", "interleaved")])
+def test_large_experts_ragged(act, layout):
+    """Experts averaging several hundred slots (the 256-row tile shape) with
+    ragged H and I and one expert holding ~40 % of all slots."""
+    T, H, I, E, K = 900, 328, 200, 4, 2
+    inp = small_inputs(T, H, I, E, K, "bf16", act, layout, seed=21, ids=skewed_ids(T, K, E, 21))
+    assert T * K // E >= 320
+    run_and_compare(inp, grad_dtype="bf16")
