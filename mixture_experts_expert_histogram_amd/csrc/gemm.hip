@@ -29,14 +29,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------------ helpers
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return b >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 values rounded to bf16 (nearest, ties to even) and packed, low
+// half first: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 template <typename T> __device__ __forceinline__ void store_val(T* p, float v);
-template <> __device__ __forceinline__ void store_val<uint16_t>(uint16_t* p, float v) { *p = (uint16_t)bf16_bits(v); }
+template <> __device__ __forceinline__ void store_val<uint16_t>(uint16_t* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
 template <> __device__ __forceinline__ void store_val<float>(float* p, float v) { *p = v; }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
@@ -77,7 +80,7 @@ __device__ __forceinline__ int acc_col4(int vg, int lane) { return (vg << 3) + (
 
 template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
-  *(uint2*)p = make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+  *(uint2*)p = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
 }
 template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
   *(float4*)p = make_float4(a, b, c, d);
@@ -85,8 +88,7 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
 // interleaved pairs (g0 u0 g1 u1 g2 u2 g3 u3)
 template <typename T> __device__ __forceinline__ void store4x2(T* p, const float* g, const float* u);
 template <> __device__ __forceinline__ void store4x2<uint16_t>(uint16_t* p, const float* g, const float* u) {
-  *(uint4*)p = make_uint4(bf16_bits(g[0]) | (bf16_bits(u[0]) << 16), bf16_bits(g[1]) | (bf16_bits(u[1]) << 16),
-                          bf16_bits(g[2]) | (bf16_bits(u[2]) << 16), bf16_bits(g[3]) | (bf16_bits(u[3]) << 16));
+  *(uint4*)p = make_uint4(pack_bf16(g[0], u[0]), pack_bf16(g[1], u[1]), pack_bf16(g[2], u[2]), pack_bf16(g[3], u[3]));
 }
 template <> __device__ __forceinline__ void store4x2<float>(float* p, const float* g, const float* u) {
   *(float4*)p = make_float4(g[0], u[0], g[1], u[1]);
@@ -572,6 +574,7 @@ struct GArgs {
   float limit, alpha;
   int ntn, ntm, nparts;
   int big;   // weight grads: experts with more positions than this are split over the XCDs
+  int small_max;   // weight grads: the tiled kernel takes only experts with more positions (-1: all)
   // Gate/up rows of the weights (gu_*) and of their gradients (dgu_*): row j of
   // expert e's gate (up) projection starts gu_es*e + gu_rs*j elements after
   // gu_g (gu_u).  Fused [E,2I,H] concatenated: (W, W + I*H, 2IH, H);
@@ -977,6 +980,15 @@ struct WgradList {
     const WgradPlan p = wgrad_plan(g.ntm, g.ntn);
     tiles = p.tiles;
     tpx = p.tpx;
+    if (g.small_max >= 0) {   // only the leading experts with more than small_max positions
+      int l = 0, h = E;
+      while (l < h) {
+        const int mid = (l + h) >> 1;
+        const int e = tab->order[mid];
+        if (tab->offsets[e + 1] - tab->offsets[e] > g.small_max) l = mid + 1; else h = mid;
+      }
+      E = l;
+    }
     int l = 0, h = E;   // nb = leading experts (descending count) with count > big
     while (l < h) {
       const int mid = (l + h) >> 1;
@@ -1237,6 +1249,279 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
   }
 }
 
+// ------------------------------------------------ weight gradients, resident
+// Experts with at most KMAX positions (bf16 operands).  The product
+// dW[e] = A_e^T B_e (M x N) contracts over the expert's c <= KMAX positions,
+// so a dW tile carries only 2c flops per element and the kernel is bound by
+// the dW write stream.  A tiled kernel reloads both operands for every
+// 128 x 128 output tile and stages the tile through LDS, which moves several
+// times more LDS bytes than the tile writes to HBM.  Here:
+// * A work item is (expert, 128-column block of N).  Each of the 4 MMA waves
+//   (2 x 2, 64 x 64 of the output each) reads its 64 columns of B_e x all c
+//   positions into registers once per item (the resident operand: up to
+//   KMAX/2 bf16 per lane per 32 columns).
+// * The item then sweeps M in 128-row steps: 4 loader waves copy the A_e
+//   tile (c positions x 128 rows of M, [k][128] rows with the transposing-read
+//   swizzle) into one of two LDS buffers while the MMA waves multiply the
+//   other, one barrier per tile.  Loaders only load and MMA waves only store,
+//   so neither waits on the other's memory counter.
+// * The MMA waves store dW straight from the accumulators (8 or 16 bytes per
+//   lane, a row's 64 columns completed by 8 consecutive stores).
+// * An expert without positions stores zeros and touches no LDS.
+// Items of one expert go to one XCD, dealt to its workgroups in order, so the
+// workgroups of an XCD sweep the same A_e tiles at about the same time and
+// share them in L2.
+constexpr int kResThreads = 512;   // 4 MMA waves + 4 loader waves
+
+// Workgroup barrier that orders LDS only: the wave's LDS operations complete,
+// then s_barrier.  __syncthreads() also waits for the wave's global stores,
+// which would hold the MMA waves at every barrier until their dW stores of
+// the previous step are acknowledged.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+constexpr int kResCols = 128;      // N columns per item, M rows per step
+
+struct ResItem {
+  int e, off, cnt, nkk, n0;
+};
+
+template <int KMAX>
+struct ResList {
+  const WgradTables* tab;
+  int first, nx, nnb, count, x, K;
+  __device__ __forceinline__ void init(const GArgs& g, const WgradTables* t, int N) {
+    tab = t;
+    int l = 0, h = g.E;   // first = experts (descending count) with more than KMAX positions
+    while (l < h) {
+      const int mid = (l + h) >> 1;
+      const int e = tab->order[mid];
+      if (tab->offsets[e + 1] - tab->offsets[e] > KMAX) l = mid + 1; else h = mid;
+    }
+    first = l;
+    x = blockIdx.x & 7;
+    K = gridDim.x >> 3;
+    const int nsmall = g.E - first;
+    nx = nsmall > x ? (nsmall - x + 7) / 8 : 0;   // experts first + x + 8q of this XCD
+    nnb = (N + kResCols - 1) / kResCols;
+    count = nx * nnb;
+  }
+  __device__ __forceinline__ ResItem item(int i) const {
+    const int q = i / nnb;
+    ResItem it;   // wave-uniform (the tables are read from LDS)
+    it.e = __builtin_amdgcn_readfirstlane(tab->order[first + x + 8 * q]);
+    it.off = __builtin_amdgcn_readfirstlane(tab->offsets[it.e]);
+    it.cnt = __builtin_amdgcn_readfirstlane(tab->offsets[it.e + 1]) - it.off;
+    it.nkk = (it.cnt + 15) >> 4;
+    it.n0 = (i - q * nnb) * kResCols;
+    return it;
+  }
+};
+
+// LDS byte offset of 16-byte chunk ch (8 columns) of k-row kr in a [k][128]
+// bf16 tile (the layout frag_n reads).
+__device__ __forceinline__ int res_lds_off(int kr, int ch) { return kr * 256 + ((ch ^ ((kr & 3) << 2)) << 4); }
+
+template <bool GATE_UP, typename OutT, int KMAX>
+__global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
+  using C = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // frag_n reads [k][128] bf16 tiles
+  constexpr int NKK = KMAX / 16;
+  constexpr int TILE_BYTES = KMAX * kResCols * 2;
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
+  __shared__ WgradTables tab;
+  const int H = g.H, I = g.I;
+  const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
+  const int lda = M, ldb = N;   // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
+  for (int i = threadIdx.x; i <= g.E; i += kResThreads) {
+    if (i < g.E) tab.order[i] = g.expert_order[i];
+    tab.offsets[i] = g.offsets[i];
+  }
+  __syncthreads();
+  ResList<KMAX> list;
+  list.init(g, &tab, N);
+  const int ntm = (M + kResCols - 1) / kResCols;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w0 = blockIdx.x >> 3;
+
+  // Tiles of this workgroup: items with positions in list order, each its B
+  // block (tile 0) then its ntm A tiles.
+  int total = 0;
+  for (int i = w0; i < list.count; i += list.K) {
+    const int c = list.item(i).cnt;
+    total += c > 0 ? ntm + 1 : 0;
+  }
+  if (wave >= 4) {
+    // ---------------- loader waves
+    // Two groups of two waves take alternate tiles, so a group issues the
+    // loads of its next tile two barrier intervals before that tile is due
+    // (one register set per group; a wave waits only for its own loads).
+    const int grp = (wave - 4) >> 1;
+    const int t = threadIdx.x - 256 - 128 * grp;
+    const int ch = t & 15, kr0 = t >> 4;   // 16-byte chunk of the row; rows kr0 + 8 r
+    const uint16_t* Ag = (const uint16_t*)g.A;
+    const uint16_t* Bg = (const uint16_t*)g.B;
+    uint4 reg[2 * NKK];
+    uint32_t okm = 0;
+    int rounds = 0;
+    // cursor: tile u of item i (u = 0: the item's B block, u = 1 + j: A rows j*128..)
+    int i = w0, u = 0;
+    ResItem it;
+    auto settle = [&]() {   // move to the first tile at or after (i, u)
+      while (i < list.count) {
+        it = list.item(i);
+        if (it.cnt > 0 && u <= ntm) return;
+        i += list.K;
+        u = 0;
+      }
+    };
+    auto advance = [&]() { ++u; settle(); };
+    auto load = [&]() {
+      const uint16_t* src = u == 0 ? Bg + (size_t)it.off * ldb + it.n0 : Ag + (size_t)it.off * lda + (u - 1) * kResCols;
+      const int ld = u == 0 ? ldb : lda;
+      const int cols = u == 0 ? N - it.n0 : M - (u - 1) * kResCols;
+      const bool col_ok = ch * 8 < cols;
+      rounds = 2 * it.nkk;
+      okm = 0;
+#pragma unroll
+      for (int r = 0; r < 2 * NKK; ++r) {
+        if (r < rounds) {
+          const int kr = kr0 + 8 * r;
+          const bool ok = col_ok && kr < it.cnt;
+          okm |= (uint32_t)ok << r;
+          reg[r] = *(const uint4*)(src + (ok ? (size_t)kr * ld + ch * 8 : 0));
+        }
+      }
+    };
+    auto store = [&](char* buf) {
+#pragma unroll
+      for (int r = 0; r < 2 * NKK; ++r)
+        if (r < rounds) *(uint4*)(buf + res_lds_off(kr0 + 8 * r, ch)) = masked(reg[r], (okm >> r) & 1);
+    };
+    settle();
+    if (grp == 1) advance();
+    if (grp < total) load();
+    for (int tile = 0; tile < total; ++tile) {
+      if ((tile & 1) == grp) {
+        store(smem_raw + (tile & 1) * TILE_BYTES);
+        advance();
+        advance();
+        if (tile + 2 < total) load();
+      }
+      lds_barrier();   // tile ready (and the buffer it replaced consumed)
+    }
+    return;
+  }
+
+  // ---------------- MMA waves
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  OutT* dW = (OutT*)g.out0;
+  bf16x8_t bres[2][NKK];
+  f32x16 acc[2][2];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  };
+  auto row_ptr = [&](int e, int m) -> OutT* {
+    if (GATE_UP && g.gu_sep) {   // separate dW_gate, dW_up: row m is a dZ column
+      int up, jj;
+      zcol(m, I, g.layout, up, jj);
+      return gu_row((OutT*)g.dgu_g, (OutT*)g.dgu_u, g.gu_es, g.gu_rs, e, up, jj);
+    }
+    return dW + ((size_t)e * M + m) * N;
+  };
+  // store the 64 x 64 accumulator block of M-step j of item it
+  auto store_acc = [&](const ResItem& it, int j) {
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+      const int m = j * kResCols + wm * 64 + fm * 32 + (lane & 31);
+      const bool m_ok = m < M;
+      OutT* row = row_ptr(it.e, m_ok ? m : 0);
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) {
+        if constexpr (sizeof(OutT) == 2) {
+          // Register groups 2p and 2p+1 hold columns 16p + 4h + 0..3 and
+          // 16p + 8 + 4h + 0..3 (h = lane / 32).  Swapping group 2p+1 of the
+          // lower half-wave with group 2p of the upper one gives lane h 8
+          // consecutive columns 16p + 8h + 0..7: one 16-byte store, and 32
+          // contiguous bytes per row from the two half-waves.
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const f32x16& a = acc[fm][fn];
+            const uint32_t p0 = pack_bf16(a[8 * p], a[8 * p + 1]);
+            const uint32_t p1 = pack_bf16(a[8 * p + 2], a[8 * p + 3]);
+            const uint32_t q0 = pack_bf16(a[8 * p + 4], a[8 * p + 5]);
+            const uint32_t q1 = pack_bf16(a[8 * p + 6], a[8 * p + 7]);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+            const int n = it.n0 + wn * 64 + fn * 32 + 16 * p + 8 * (lane >> 5);
+            if (m_ok && n < N) *(uint4*)(row + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          }
+        } else {
+#pragma unroll
+          for (int vg = 0; vg < 4; ++vg) {
+            const int n = it.n0 + wn * 64 + fn * 32 + acc_col4(vg, lane);
+            if (m_ok && n < N)
+              store4<OutT>(row + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
+                           acc[fm][fn][vg * 4 + 3]);
+          }
+        }
+      }
+    }
+  };
+  // Experts without positions first (zeros in whole 16-byte chunks, no LDS),
+  // while no resident operand is live.
+  for (int i = w0; i < list.count; i += list.K) {
+    const ResItem it = list.item(i);
+    if (it.cnt != 0) continue;
+    constexpr int VPC = 16 / (int)sizeof(OutT), CPR = kResCols / VPC;
+    const int c = (threadIdx.x % CPR) * VPC;
+    if (c < N - it.n0)
+      for (int m = threadIdx.x / CPR; m < M; m += 256 / CPR)
+        *(uint4*)(row_ptr(it.e, m) + it.n0 + c) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  int tile = 0;
+  for (int i = w0; i < list.count; i += list.K) {
+    const ResItem it = list.item(i);
+    if (it.cnt == 0) continue;
+    lds_barrier();   // B block ready
+    {
+      const uint16_t* buf = (const uint16_t*)(smem_raw + (tile & 1) * TILE_BYTES);
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          if (kk < it.nkk) bres[fn][kk] = frag_n<C>(buf, wn * 64 + fn * 32, kk, lane);
+    }
+    ++tile;
+    for (int j = 0; j < ntm; ++j, ++tile) {
+      lds_barrier();   // A tile j ready
+      const uint16_t* buf = (const uint16_t*)(smem_raw + (tile & 1) * TILE_BYTES);
+      zero_acc();
+      bf16x8_t a[2][2];
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm) a[0][fm] = frag_n<C>(buf, wm * 64 + fm * 32, 0, lane);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk < it.nkk) {
+          if (kk + 1 < it.nkk) {
+#pragma unroll
+            for (int fm = 0; fm < 2; ++fm) a[(kk + 1) & 1][fm] = frag_n<C>(buf, wm * 64 + fm * 32, kk + 1, lane);
+          }
+#pragma unroll
+          for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < 2; ++fn)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bres[fn][kk], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+        }
+      }
+      store_acc(it, j);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 using CfgB = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // bf16
 // bf16 with 192-row M-tiles (96 rows per wave): when experts average a little
@@ -1406,7 +1691,8 @@ static int device_cus() {
 }
 
 template <class C, bool GU, typename OutT>
-static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
+static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s,
+                             int small_max) {
   const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
   if (pb.S == 0) {   // no positions
     if (GU && pb.dw_up) {
@@ -1423,20 +1709,45 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
   // split experts: more than twice the mean positions per expert (and more than 4 k-steps)
   const long mean = ((long)pb.S + pb.E - 1) / pb.E;
   g.big = (int)std::max<long>(2 * mean, 4 * C::BK);
+  g.small_max = small_max;
   // one persistent workgroup per CU, a whole number per XCD
   static const int cus = device_cus();
   const long grid = (cus / 8) * 8;
-  return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s,
-                    [&] { wgrad_kernel<C, GU, OutT><<<grid, C::NT + kStoreThreads, 0, s>>>(g); });
+  const char* name = small_max >= 0 ? (GU ? "wgrad_gate_up_hot" : "wgrad_down_hot")
+                                    : (GU ? "wgrad_gate_up" : "wgrad_down");
+  return run_kernel(name, s, [&] { wgrad_kernel<C, GU, OutT><<<grid, C::NT + kStoreThreads, 0, s>>>(g); });
+}
+
+// Experts with at most this many positions take the resident-operand kernel.
+constexpr int kResKmax = 256;
+
+template <bool GU, typename OutT>
+static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
+  GArgs g = base_args(pb, 128);
+  g.A = A; g.B = B; g.out0 = dW;
+  if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
+  static const int cus = device_cus();
+  const long grid = (cus / 8) * 8;
+  return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s, [&] {
+    wgrad_res_kernel<GU, OutT, kResKmax><<<grid, kResThreads, 0, s>>>(g);
+  });
 }
 
 template <bool GU>
 static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
+  if (pb.dtype == 0 && pb.S > 0) {
+    // experts with at most kResKmax positions (and those without any), then the rest
+    hipError_t e = pb.gdtype == 0 ? wgrad_res_impl<GU, uint16_t>(pb, A, B, dW, s)
+                                  : wgrad_res_impl<GU, float>(pb, A, B, dW, s);
+    if (e != hipSuccess) return e;
+    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax)
+                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax);
+  }
   if (pb.dtype == 0)
-    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s)
-                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s);
-  return pb.gdtype == 0 ? wgrad_impl<CfgWF, GU, uint16_t>(pb, A, B, dW, s)
-                        : wgrad_impl<CfgWF, GU, float>(pb, A, B, dW, s);
+    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, -1)
+                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, -1);
+  return pb.gdtype == 0 ? wgrad_impl<CfgWF, GU, uint16_t>(pb, A, B, dW, s, -1)
+                        : wgrad_impl<CfgWF, GU, float>(pb, A, B, dW, s, -1);
 }
 
 hipError_t launch_wgrad_down(const GemmProblem& pb, const void* dY, const void* aw, void* dWd, hipStream_t s) {

@@ -323,11 +323,11 @@ hipError_t launch_route_logits(const float* logits, int T, int K, int E, int32_t
 // Combine: out[t] = sum_{k<K} Yp[inv_pos[t*K+k]] over fp32 rows, summed in k
 // order, one rounding to the storage type.  One thread owns 16 bytes of one
 // output row.
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return b >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 values rounded to bf16 (nearest, ties to even), low half first.
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <bool OUT_BF16>
@@ -354,10 +354,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     uint4 o;
     if (OUT_BF16) {
-      o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-      o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-      o.z = f32_to_bf16_bits(acc[4 % V]) | (f32_to_bf16_bits(acc[5 % V]) << 16);
-      o.w = f32_to_bf16_bits(acc[6 % V]) | (f32_to_bf16_bits(acc[7 % V]) << 16);
+      o.x = pack_bf16(acc[0], acc[1]);
+      o.y = pack_bf16(acc[2], acc[3]);
+      o.z = pack_bf16(acc[4 % V], acc[5 % V]);
+      o.w = pack_bf16(acc[6 % V], acc[7 % V]);
     } else {
       o.x = __float_as_uint(acc[0]); o.y = __float_as_uint(acc[1]);
       o.z = __float_as_uint(acc[2 % V]); o.w = __float_as_uint(acc[3 % V]);

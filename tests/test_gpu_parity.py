@@ -203,3 +203,17 @@ def test_large_experts_ragged(act, layout):
     inp = small_inputs(T, H, I, E, K, "bf16", act, layout, seed=21, ids=skewed_ids(T, K, E, 21))
     assert T * K // E >= 320
     run_and_compare(inp, grad_dtype="bf16")
+
+
+@pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
+def test_weight_grad_expert_sizes(grad_dtype):
+    """Experts of 0, 1, 16, 17, 256 and 257 slots: the resident-operand weight
+    gradient takes experts of up to 256 slots (k-slices of 16, zeros for an
+    empty expert) and the tiled one the rest; both in one call."""
+    counts = [256, 257, 1, 16, 17, 0]
+    E, K = len(counts), 1
+    T, H, I = sum(counts), 264, 200
+    rng = np.random.default_rng(31)
+    ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
+    inp = small_inputs(T, H, I, E, K, "bf16", "clamped", "interleaved", seed=31, ids=ids)
+    run_and_compare(inp, grad_dtype=grad_dtype)
