@@ -1250,24 +1250,31 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 }
 
 // ------------------------------------------------ weight gradients, resident
-// Experts with at most KMAX positions (bf16 operands).  The product
-// dW[e] = A_e^T B_e (M x N) contracts over the expert's c <= KMAX positions,
-// so a dW tile carries only 2c flops per element and the kernel is bound by
-// the dW write stream.  A tiled kernel reloads both operands for every
-// 128 x 128 output tile and stages the tile through LDS, which moves several
-// times more LDS bytes than the tile writes to HBM.  Here:
+// Experts with at most KMAX positions, bf16 operands and bf16 gradients.  The
+// product dW[e] = A_e^T B_e (M x N) contracts over the expert's c <= KMAX
+// positions, so each dW element carries only 2c flops.  The tiled kernel
+// reloads both operands for every 128 x 128 output tile and stages the tile
+// through LDS.  That moves several times more LDS bytes than the tile writes
+// to HBM.  Here:
 // * A work item is (expert, 128-column block of N).  Each of the 4 MMA waves
 //   (2 x 2, 64 x 64 of the output each) reads its 64 columns of B_e x all c
-//   positions into registers once per item (the resident operand: up to
-//   KMAX/2 bf16 per lane per 32 columns).
-// * The item then sweeps M in 128-row steps: 4 loader waves copy the A_e
-//   tile (c positions x 128 rows of M, [k][128] rows with the transposing-read
-//   swizzle) into one of two LDS buffers while the MMA waves multiply the
-//   other, one barrier per tile.  Loaders only load and MMA waves only store,
-//   so neither waits on the other's memory counter.
-// * The MMA waves store dW straight from the accumulators (8 or 16 bytes per
-//   lane, a row's 64 columns completed by 8 consecutive stores).
-// * An expert without positions stores zeros and touches no LDS.
+//   positions into registers once per item.  This is the resident operand:
+//   up to KMAX/2 bf16 per lane per 32 columns.
+// * The item then sweeps M in 128-row steps.  The A_e tile (c positions x 128
+//   rows of M) is stored in [k][128] rows with the transposing-read swizzle,
+//   in one of two LDS buffers, while the MMA waves multiply the other.  There
+//   is one barrier per tile.
+// * Two groups of two loader waves take alternate tiles.  A group issues a
+//   tile's loads two barrier intervals before the tile is due.  Loaders only
+//   load and MMA waves only store, so neither waits on the other's memory
+//   counter.
+// * The MMA waves round the accumulators to bf16 (v_cvt_pk_bf16_f32), re-tile
+//   each 32 x 64 block through 4 KB of wave-private LDS, and store whole
+//   128-byte row segments.  A store straight from the accumulator layout
+//   touches 32 cache lines per instruction, and the resulting address traffic
+//   held up the operand loads.
+// * An expert without positions gets zeros, written before any operand is
+//   resident.
 // Items of one expert go to one XCD, dealt to its workgroups in order, so the
 // workgroups of an XCD sweep the same A_e tiles at about the same time and
 // share them in L2.
@@ -1320,13 +1327,18 @@ struct ResList {
 // bf16 tile (the layout frag_n reads).
 __device__ __forceinline__ int res_lds_off(int kr, int ch) { return kr * 256 + ((ch ^ ((kr & 3) << 2)) << 4); }
 
-template <bool GATE_UP, typename OutT, int KMAX>
+template <bool GATE_UP, int KMAX>
 __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
+  using OutT = uint16_t;   // bf16 gradients
   using C = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // frag_n reads [k][128] bf16 tiles
   constexpr int NKK = KMAX / 16;
   constexpr int TILE_BYTES = KMAX * kResCols * 2;
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
   __shared__ WgradTables tab;
+  // per MMA wave, 32 rows x 128 bytes to re-tile a 32 x 64 block of the
+  // accumulators into whole 128-byte row segments
+  constexpr int STAGE_WAVE = 32 * 128;
+  __shared__ __attribute__((aligned(16))) char stage_raw[4 * STAGE_WAVE];
   const int H = g.H, I = g.I;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
   const int lda = M, ldb = N;   // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
@@ -1413,6 +1425,11 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   // ---------------- MMA waves
   const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  char* stage = stage_raw + wave * STAGE_WAVE;
+  // byte offset of 16-byte chunk c (0..7) of staging row r: chunks XOR-ed
+  // with (r/2)%8, so 16 lanes writing one chunk of 16 rows, or reading two
+  // whole rows, touch 16 distinct bank groups
+  auto stage_off = [](int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); };
   OutT* dW = (OutT*)g.out0;
   bf16x8_t bres[2][NKK];
   f32x16 acc[2][2];
@@ -1436,41 +1453,42 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   auto store_acc = [&](const ResItem& it, int j) {
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm) {
-      const int m = j * kResCols + wm * 64 + fm * 32 + (lane & 31);
-      const bool m_ok = m < M;
-      OutT* row = row_ptr(it.e, m_ok ? m : 0);
+      __builtin_amdgcn_sched_barrier(0);   // one 32-row block at a time (register pressure)
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn) {
-        if constexpr (sizeof(OutT) == 2) {
-          // Register groups 2p and 2p+1 hold columns 16p + 4h + 0..3 and
-          // 16p + 8 + 4h + 0..3 (h = lane / 32).  Swapping group 2p+1 of the
-          // lower half-wave with group 2p of the upper one gives lane h 8
-          // consecutive columns 16p + 8h + 0..7: one 16-byte store, and 32
-          // contiguous bytes per row from the two half-waves.
+        // Register groups 2p and 2p+1 hold columns 16p + 4h + 0..3 and
+        // 16p + 8 + 4h + 0..3 (h = lane / 32).  Swapping group 2p+1 of the
+        // lower half-wave with group 2p of the upper one gives lane h 8
+        // consecutive columns 16p + 8h + 0..7 (16-byte chunk 4fn + 2p + h
+        // of the row), written to the wave's staging rows.
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const f32x16& a = acc[fm][fn];
-            const uint32_t p0 = pack_bf16(a[8 * p], a[8 * p + 1]);
-            const uint32_t p1 = pack_bf16(a[8 * p + 2], a[8 * p + 3]);
-            const uint32_t q0 = pack_bf16(a[8 * p + 4], a[8 * p + 5]);
-            const uint32_t q1 = pack_bf16(a[8 * p + 6], a[8 * p + 7]);
-            const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
-            const int n = it.n0 + wn * 64 + fn * 32 + 16 * p + 8 * (lane >> 5);
-            if (m_ok && n < N) *(uint4*)(row + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-          }
-        } else {
-#pragma unroll
-          for (int vg = 0; vg < 4; ++vg) {
-            const int n = it.n0 + wn * 64 + fn * 32 + acc_col4(vg, lane);
-            if (m_ok && n < N)
-              store4<OutT>(row + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
-                           acc[fm][fn][vg * 4 + 3]);
-          }
+        for (int p = 0; p < 2; ++p) {
+          const f32x16& a = acc[fm][fn];
+          const uint32_t p0 = pack_bf16(a[8 * p], a[8 * p + 1]);
+          const uint32_t p1 = pack_bf16(a[8 * p + 2], a[8 * p + 3]);
+          const uint32_t q0 = pack_bf16(a[8 * p + 4], a[8 * p + 5]);
+          const uint32_t q1 = pack_bf16(a[8 * p + 6], a[8 * p + 7]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+          const int r = lane & 31, c = 4 * fn + 2 * p + (lane >> 5);
+          *(uint4*)(stage + stage_off(r, c)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
         }
+      }
+      // 8 lanes per staged row: each store instruction writes 8 whole
+      // 128-byte row segments (a quarter of the cache lines a store from
+      // the accumulator layout touches).
+      const int c = lane & 7;
+      const int n = it.n0 + wn * 64 + c * 8;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = q * 8 + (lane >> 3);
+        const uint4 v = *(const uint4*)(stage + stage_off(r, c));
+        const int m = j * kResCols + wm * 64 + fm * 32 + r;
+        if (m < M && n < N) *(uint4*)(row_ptr(it.e, m) + n) = v;
       }
     }
   };
+
   // Experts without positions first (zeros in whole 16-byte chunks, no LDS),
   // while no resident operand is live.
   for (int i = w0; i < list.count; i += list.K) {
@@ -1719,29 +1737,30 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
 }
 
 // Experts with at most this many positions take the resident-operand kernel.
-constexpr int kResKmax = 256;
+constexpr int kResKmax = 208;
 
-template <bool GU, typename OutT>
+template <bool GU>
 static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
   GArgs g = base_args(pb, 128);
   g.A = A; g.B = B; g.out0 = dW;
-  if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
+  if (GU) set_gu(g, pb, nullptr, dW, 2);
   static const int cus = device_cus();
   const long grid = (cus / 8) * 8;
   return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s, [&] {
-    wgrad_res_kernel<GU, OutT, kResKmax><<<grid, kResThreads, 0, s>>>(g);
+    wgrad_res_kernel<GU, kResKmax><<<grid, kResThreads, 0, s>>>(g);
   });
 }
 
 template <bool GU>
 static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
-  if (pb.dtype == 0 && pb.S > 0) {
-    // experts with at most kResKmax positions (and those without any), then the rest
-    hipError_t e = pb.gdtype == 0 ? wgrad_res_impl<GU, uint16_t>(pb, A, B, dW, s)
-                                  : wgrad_res_impl<GU, float>(pb, A, B, dW, s);
+  if (pb.dtype == 0 && pb.gdtype == 0 && pb.S > 0) {
+    // bf16 gradients: experts with at most kResKmax positions (and those
+    // without any), then the rest.  fp32 gradients stay on the tiled kernel,
+    // whose staged whole-row stores write them faster than the accumulator
+    // layout does.
+    const hipError_t e = wgrad_res_impl<GU>(pb, A, B, dW, s);
     if (e != hipSuccess) return e;
-    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax)
-                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax);
+    return wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax);
   }
   if (pb.dtype == 0)
     return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, -1)
