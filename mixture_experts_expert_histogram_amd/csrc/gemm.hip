@@ -1285,7 +1285,8 @@ constexpr int kResThreads = 512;   // 4 MMA waves + 4 loader waves
 // which would hold the MMA waves at every barrier until their dW stores of
 // the previous step are acknowledged.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-constexpr int kResCols = 128;      // N columns per item, M rows per step
+constexpr int kResN = 256;   // N columns per item (64 per MMA wave)
+constexpr int kResM = 64;    // M rows per step
 
 struct ResItem {
   int e, off, cnt, nkk, n0;
@@ -1308,7 +1309,7 @@ struct ResList {
     K = gridDim.x >> 3;
     const int nsmall = g.E - first;
     nx = nsmall > x ? (nsmall - x + 7) / 8 : 0;   // experts first + x + 8q of this XCD
-    nnb = (N + kResCols - 1) / kResCols;
+    nnb = (N + kResN - 1) / kResN;
     count = nx * nnb;
   }
   __device__ __forceinline__ ResItem item(int i) const {
@@ -1318,21 +1319,42 @@ struct ResList {
     it.off = __builtin_amdgcn_readfirstlane(tab->offsets[it.e]);
     it.cnt = __builtin_amdgcn_readfirstlane(tab->offsets[it.e + 1]) - it.off;
     it.nkk = (it.cnt + 15) >> 4;
-    it.n0 = (i - q * nnb) * kResCols;
+    it.n0 = (i - q * nnb) * kResN;
     return it;
   }
 };
 
-// LDS byte offset of 16-byte chunk ch (8 columns) of k-row kr in a [k][128]
-// bf16 tile (the layout frag_n reads).
-__device__ __forceinline__ int res_lds_off(int kr, int ch) { return kr * 256 + ((ch ^ ((kr & 3) << 2)) << 4); }
+// [k][64] bf16 operand tiles: 128-byte k-rows whose 16-byte chunks are XOR-ed
+// with 4*((k/2)%2).  A transposing fragment read takes 4 consecutive k-rows
+// x 32 bytes per 16 lanes; with the swizzle the 32 lanes of a half-wave hit
+// 8 distinct 32-byte slots of the 256-byte bank window.
+__device__ __forceinline__ int res_lds_off(int kr, int ch) { return kr * 128 + ((ch ^ (((kr >> 1) & 1) << 2)) << 4); }
+
+// 32 columns (cb .. cb+31) x 16 k of a [k][64] tile: lane -> column cb + lane%32,
+// k = kk*16 + 8*(lane/32) + 0..7 (the K-contiguous fragment layout).
+__device__ __forceinline__ bf16x8_t frag_k64(const char* tile, int cb, int kk, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = cb + ((g & 1) << 4) + ((s & 3) << 2);
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  const lds_char* base = (const lds_char*)tile;
+  s16x4_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int krow = kk * 16 + ((g >> 1) << 3) + h * 4 + (s >> 2);
+    r[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + res_lds_off(krow, chunk) + within));
+  }
+  bf16x8_t out;
+  s16x4_t* o = (s16x4_t*)&out;
+  o[0] = r[0];
+  o[1] = r[1];
+  return out;
+}
 
 template <bool GATE_UP, int KMAX>
 __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   using OutT = uint16_t;   // bf16 gradients
-  using C = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // frag_n reads [k][128] bf16 tiles
   constexpr int NKK = KMAX / 16;
-  constexpr int TILE_BYTES = KMAX * kResCols * 2;
+  constexpr int TILE_BYTES = KMAX * kResM * 2;
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
   __shared__ WgradTables tab;
   // per MMA wave, 32 rows x 128 bytes to re-tile a 32 x 64 block of the
@@ -1349,16 +1371,17 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   __syncthreads();
   ResList<KMAX> list;
   list.init(g, &tab, N);
-  const int ntm = (M + kResCols - 1) / kResCols;
+  const int ntm = (M + kResM - 1) / kResM;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int w0 = blockIdx.x >> 3;
 
-  // Tiles of this workgroup: items with positions in list order, each its B
-  // block (tile 0) then its ntm A tiles.
+  // Tiles of this workgroup: items with positions in list order; per item
+  // 4 B tiles (the 64-column slices of the item's B block, one per MMA
+  // wave), then its ntm A tiles.
   int total = 0;
   for (int i = w0; i < list.count; i += list.K) {
     const int c = list.item(i).cnt;
-    total += c > 0 ? ntm + 1 : 0;
+    total += c > 0 ? ntm + 4 : 0;
   }
   if (wave >= 4) {
     // ---------------- loader waves
@@ -1367,35 +1390,43 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
     // (one register set per group; a wave waits only for its own loads).
     const int grp = (wave - 4) >> 1;
     const int t = threadIdx.x - 256 - 128 * grp;
-    const int ch = t & 15, kr0 = t >> 4;   // 16-byte chunk of the row; rows kr0 + 8 r
+    const int ch = t & 7, kr0 = t >> 3;   // 16-byte chunk of the row; rows kr0 + 16 r
     const uint16_t* Ag = (const uint16_t*)g.A;
     const uint16_t* Bg = (const uint16_t*)g.B;
-    uint4 reg[2 * NKK];
+    uint4 reg[NKK];
     uint32_t okm = 0;
     int rounds = 0;
-    // cursor: tile u of item i (u = 0: the item's B block, u = 1 + j: A rows j*128..)
+    // cursor: tile u of item i (u < 4: B columns n0 + 64u.., else A rows (u-4)*64..)
     int i = w0, u = 0;
     ResItem it;
     auto settle = [&]() {   // move to the first tile at or after (i, u)
       while (i < list.count) {
         it = list.item(i);
-        if (it.cnt > 0 && u <= ntm) return;
+        if (it.cnt > 0 && u < ntm + 4) return;
         i += list.K;
         u = 0;
       }
     };
     auto advance = [&]() { ++u; settle(); };
     auto load = [&]() {
-      const uint16_t* src = u == 0 ? Bg + (size_t)it.off * ldb + it.n0 : Ag + (size_t)it.off * lda + (u - 1) * kResCols;
-      const int ld = u == 0 ? ldb : lda;
-      const int cols = u == 0 ? N - it.n0 : M - (u - 1) * kResCols;
+      const uint16_t* src;
+      int ld, cols;
+      if (u < 4) {
+        cols = N - (it.n0 + 64 * u);
+        src = Bg + (size_t)it.off * ldb + (cols > 0 ? it.n0 + 64 * u : 0);
+        ld = ldb;
+      } else {
+        cols = M - (u - 4) * kResM;
+        src = Ag + (size_t)it.off * lda + (u - 4) * kResM;
+        ld = lda;
+      }
       const bool col_ok = ch * 8 < cols;
-      rounds = 2 * it.nkk;
+      rounds = it.nkk;
       okm = 0;
 #pragma unroll
-      for (int r = 0; r < 2 * NKK; ++r) {
+      for (int r = 0; r < NKK; ++r) {
         if (r < rounds) {
-          const int kr = kr0 + 8 * r;
+          const int kr = kr0 + 16 * r;
           const bool ok = col_ok && kr < it.cnt;
           okm |= (uint32_t)ok << r;
           reg[r] = *(const uint4*)(src + (ok ? (size_t)kr * ld + ch * 8 : 0));
@@ -1404,8 +1435,8 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
     };
     auto store = [&](char* buf) {
 #pragma unroll
-      for (int r = 0; r < 2 * NKK; ++r)
-        if (r < rounds) *(uint4*)(buf + res_lds_off(kr0 + 8 * r, ch)) = masked(reg[r], (okm >> r) & 1);
+      for (int r = 0; r < NKK; ++r)
+        if (r < rounds) *(uint4*)(buf + res_lds_off(kr0 + 16 * r, ch)) = masked(reg[r], (okm >> r) & 1);
     };
     settle();
     if (grp == 1) advance();
@@ -1424,23 +1455,14 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
 
   // ---------------- MMA waves
   const int lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  OutT* dW = (OutT*)g.out0;
   char* stage = stage_raw + wave * STAGE_WAVE;
   // byte offset of 16-byte chunk c (0..7) of staging row r: chunks XOR-ed
   // with (r/2)%8, so 16 lanes writing one chunk of 16 rows, or reading two
   // whole rows, touch 16 distinct bank groups
   auto stage_off = [](int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); };
-  OutT* dW = (OutT*)g.out0;
   bf16x8_t bres[2][NKK];
   f32x16 acc[2][2];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
-  };
   auto row_ptr = [&](int e, int m) -> OutT* {
     if (GATE_UP && g.gu_sep) {   // separate dW_gate, dW_up: row m is a dZ column
       int up, jj;
@@ -1478,24 +1500,23 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
       // 128-byte row segments (a quarter of the cache lines a store from
       // the accumulator layout touches).
       const int c = lane & 7;
-      const int n = it.n0 + wn * 64 + c * 8;
+      const int n = it.n0 + wave * 64 + c * 8;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = q * 8 + (lane >> 3);
         const uint4 v = *(const uint4*)(stage + stage_off(r, c));
-        const int m = j * kResCols + wm * 64 + fm * 32 + r;
+        const int m = j * kResM + fm * 32 + r;
         if (m < M && n < N) *(uint4*)(row_ptr(it.e, m) + n) = v;
       }
     }
   };
-
   // Experts without positions first (zeros in whole 16-byte chunks, no LDS),
   // while no resident operand is live.
   for (int i = w0; i < list.count; i += list.K) {
     const ResItem it = list.item(i);
     if (it.cnt != 0) continue;
-    constexpr int VPC = 16 / (int)sizeof(OutT), CPR = kResCols / VPC;
-    const int c = (threadIdx.x % CPR) * VPC;
+    constexpr int CPR = kResN / 8;   // 16-byte chunks per row of the item
+    const int c = (threadIdx.x % CPR) * 8;
     if (c < N - it.n0)
       for (int m = threadIdx.x / CPR; m < M; m += 256 / CPR)
         *(uint4*)(row_ptr(it.e, m) + it.n0 + c) = make_uint4(0u, 0u, 0u, 0u);
@@ -1504,35 +1525,38 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   for (int i = w0; i < list.count; i += list.K) {
     const ResItem it = list.item(i);
     if (it.cnt == 0) continue;
-    lds_barrier();   // B block ready
-    {
-      const uint16_t* buf = (const uint16_t*)(smem_raw + (tile & 1) * TILE_BYTES);
+    // B slices: wave q reads its 64 columns when slice q is in LDS
 #pragma unroll
-      for (int fn = 0; fn < 2; ++fn)
+    for (int q = 0; q < 4; ++q, ++tile) {
+      lds_barrier();   // B slice q ready
+      if (wave == q) {
+        const char* buf = smem_raw + (tile & 1) * TILE_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          if (kk < it.nkk) bres[fn][kk] = frag_n<C>(buf, wn * 64 + fn * 32, kk, lane);
+        for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            if (kk < it.nkk) bres[fn][kk] = frag_k64(buf, fn * 32, kk, lane);
+      }
     }
-    ++tile;
     for (int j = 0; j < ntm; ++j, ++tile) {
       lds_barrier();   // A tile j ready
-      const uint16_t* buf = (const uint16_t*)(smem_raw + (tile & 1) * TILE_BYTES);
-      zero_acc();
+      const char* buf = smem_raw + (tile & 1) * TILE_BYTES;
       bf16x8_t a[2][2];
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) a[0][fm] = frag_n<C>(buf, wm * 64 + fm * 32, 0, lane);
+      for (int fm = 0; fm < 2; ++fm) a[0][fm] = frag_k64(buf, fm * 32, 0, lane);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         if (kk < it.nkk) {
           if (kk + 1 < it.nkk) {
 #pragma unroll
-            for (int fm = 0; fm < 2; ++fm) a[(kk + 1) & 1][fm] = frag_n<C>(buf, wm * 64 + fm * 32, kk + 1, lane);
+            for (int fm = 0; fm < 2; ++fm) a[(kk + 1) & 1][fm] = frag_k64(buf, fm * 32, kk + 1, lane);
           }
 #pragma unroll
           for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
             for (int fn = 0; fn < 2; ++fn)
-              acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bres[fn][kk], a[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bres[fn][kk], a[kk & 1][fm],
+                                                                     kk == 0 ? f32x16{} : acc[fm][fn], 0, 0, 0);
         }
       }
       store_acc(it, j);
@@ -1737,7 +1761,7 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
 }
 
 // Experts with at most this many positions take the resident-operand kernel.
-constexpr int kResKmax = 208;
+constexpr int kResKmax = 240;
 
 template <bool GU>
 static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
