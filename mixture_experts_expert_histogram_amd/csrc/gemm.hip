@@ -1357,9 +1357,9 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   constexpr int TILE_BYTES = KMAX * kResM * 2;
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
   __shared__ WgradTables tab;
-  // per MMA wave, 32 rows x 128 bytes to re-tile a 32 x 64 block of the
-  // accumulators into whole 128-byte row segments
-  constexpr int STAGE_WAVE = 32 * 128;
+  // per MMA wave, two buffers of 64 rows x 128 bytes to re-tile a step's
+  // 64 x 64 accumulator block into whole 128-byte row segments
+  constexpr int STAGE_BUF = 64 * 128, STAGE_WAVE = 2 * STAGE_BUF;
   __shared__ __attribute__((aligned(16))) char stage_raw[4 * STAGE_WAVE];
   const int H = g.H, I = g.I;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
@@ -1471,18 +1471,21 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
     }
     return dW + ((size_t)e * M + m) * N;
   };
-  // store the 64 x 64 accumulator block of M-step j of item it
-  auto store_acc = [&](const ResItem& it, int j) {
+  // The 64 x 64 accumulator block of a step is rounded to bf16 and written to
+  // the wave's staging rows (two buffers of 2 x 32 rows x 128 bytes); its
+  // global stores are issued one per k-slice during the next step's MFMAs, so
+  // the store stream drains while the matrix cores work instead of in a
+  // burst that stalls the wave.
+  auto stage_acc = [&](char* st) {
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
-      __builtin_amdgcn_sched_barrier(0);   // one 32-row block at a time (register pressure)
+    for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn) {
         // Register groups 2p and 2p+1 hold columns 16p + 4h + 0..3 and
         // 16p + 8 + 4h + 0..3 (h = lane / 32).  Swapping group 2p+1 of the
         // lower half-wave with group 2p of the upper one gives lane h 8
         // consecutive columns 16p + 8h + 0..7 (16-byte chunk 4fn + 2p + h
-        // of the row), written to the wave's staging rows.
+        // of the row).
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const f32x16& a = acc[fm][fn];
@@ -1492,23 +1495,22 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
           const uint32_t q1 = pack_bf16(a[8 * p + 6], a[8 * p + 7]);
           const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
-          const int r = lane & 31, c = 4 * fn + 2 * p + (lane >> 5);
-          *(uint4*)(stage + stage_off(r, c)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          const int r = fm * 32 + (lane & 31), c = 4 * fn + 2 * p + (lane >> 5);
+          *(uint4*)(st + stage_off(r, c)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
         }
       }
-      // 8 lanes per staged row: each store instruction writes 8 whole
-      // 128-byte row segments (a quarter of the cache lines a store from
-      // the accumulator layout touches).
-      const int c = lane & 7;
-      const int n = it.n0 + wave * 64 + c * 8;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = q * 8 + (lane >> 3);
-        const uint4 v = *(const uint4*)(stage + stage_off(r, c));
-        const int m = j * kResM + fm * 32 + r;
-        if (m < M && n < N) *(uint4*)(row_ptr(it.e, m) + n) = v;
-      }
-    }
+  };
+  // Pending staged block: rows pj*64.., columns pn0 + wave*64.. of expert pe.
+  int pe = 0, pj = 0, pn0 = 0;
+  bool pending = false;
+  const char* pst = stage;
+  // Store q (0..7) of the pending block: staged rows 8q .. 8q+7, 8 lanes per
+  // row, one whole 128-byte row segment each.
+  auto store_step = [&](int q) {
+    const int r = q * 8 + (lane >> 3), c = lane & 7;
+    const uint4 v = *(const uint4*)(pst + stage_off(r, c));
+    const int m = pj * kResM + r, n = pn0 + wave * 64 + c * 8;
+    if (m < M && n < N) *(uint4*)(row_ptr(pe, m) + n) = v;
   };
   // Experts without positions first (zeros in whole 16-byte chunks, no LDS),
   // while no resident operand is live.
@@ -1557,11 +1559,23 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
             for (int fn = 0; fn < 2; ++fn)
               acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bres[fn][kk], a[kk & 1][fm],
                                                                      kk == 0 ? f32x16{} : acc[fm][fn], 0, 0, 0);
+          if (kk < 8 && pending) store_step(kk);
         }
       }
-      store_acc(it, j);
+      if (pending)
+        for (int q = it.nkk; q < 8; ++q) store_step(q);
+      // stage this step's block in the other buffer; it is stored during the next step
+      char* st = stage + (pst == stage ? STAGE_BUF : 0);
+      stage_acc(st);
+      pst = st;
+      pe = it.e;
+      pj = j;
+      pn0 = it.n0;
+      pending = true;
     }
   }
+  if (pending)
+    for (int q = 0; q < 8; ++q) store_step(q);
 }
 
 // ------------------------------------------------------------------ host side
