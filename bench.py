@@ -97,6 +97,7 @@ def measured_traffic(kernel, workload, grad_dtype):
 
 
 # ------------------------------------------------------------------ per-kernel model
+RES_KMAX = 240   # the resident-operand weight gradient's limit (positions per expert)
 def kernel_model(wl, counts, grad_bytes):
     """Algorithmic bytes and flops of one launch of each kernel.
 
@@ -114,10 +115,27 @@ def kernel_model(wl, counts, grad_bytes):
         "combine": (S * H * 4 + T * H * eb + S * 4, 0.0),
         "down_dgrad_glu_bwd": (Wd + T * H * eb + S * 2 * I * 4 + S * 2 * I * eb + S * I * eb, 2.0 * S * H * I),
         "gate_up_dgrad": (Wgu + S * 2 * I * eb + S * H * 4, 4.0 * S * H * I),
-        "wgrad_down": (T * H * eb + S * I * eb + wl.E * H * I * grad_bytes, 2.0 * S * H * I),
-        "wgrad_gate_up": (S * 2 * I * eb + T * H * eb + wl.E * 2 * I * H * grad_bytes, 4.0 * S * H * I),
         "topkw_reduce": (S * 4 * 2, 0.0),
     }
+    # Weight gradients.  With bf16 operands and bf16 gradients, experts with at
+    # most RES_KMAX positions (and those without any) take the resident-operand
+    # kernel, named wgrad_down / wgrad_gate_up, and the rest the tiled kernel,
+    # named *_hot; otherwise the tiled kernel takes every expert under the
+    # plain names.  Token-row reads are prorated by the positions each covers.
+    def wgrad(sel):
+        s_part = int(counts[sel].sum())
+        e_part = int(sel.sum())
+        tok = s_part / S if S else 0.0
+        down = (tok * T * H * eb + s_part * I * eb + e_part * H * I * grad_bytes, 2.0 * s_part * H * I)
+        gu = (s_part * 2 * I * eb + tok * T * H * eb + e_part * 2 * I * H * grad_bytes, 4.0 * s_part * H * I)
+        return down, gu
+    if wl.dtype == "bf16" and grad_bytes == 2:
+        small = counts <= RES_KMAX
+        m["wgrad_down"], m["wgrad_gate_up"] = wgrad(small)
+        if (~small).any():
+            m["wgrad_down_hot"], m["wgrad_gate_up_hot"] = wgrad(~small)
+    else:
+        m["wgrad_down"], m["wgrad_gate_up"] = wgrad(counts >= 0)
     return m
 
 

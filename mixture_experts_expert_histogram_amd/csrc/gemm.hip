@@ -1505,12 +1505,14 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   bool pending = false;
   const char* pst = stage;
   // Store q (0..7) of the pending block: staged rows 8q .. 8q+7, 8 lanes per
-  // row, one whole 128-byte row segment each.
+  // row, one whole 128-byte row segment each, non-temporal (dW is not read
+  // again here, so it need not displace the operand tiles in L2).
   auto store_step = [&](int q) {
     const int r = q * 8 + (lane >> 3), c = lane & 7;
     const uint4 v = *(const uint4*)(pst + stage_off(r, c));
     const int m = pj * kResM + r, n = pn0 + wave * 64 + c * 8;
-    if (m < M && n < N) *(uint4*)(row_ptr(pe, m) + n) = v;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    if (m < M && n < N) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)(row_ptr(pe, m) + n));
   };
   // Experts without positions first (zeros in whole 16-byte chunks, no LDS),
   // while no resident operand is live.
