@@ -1325,10 +1325,13 @@ struct ResList {
 };
 
 // [k][64] bf16 operand tiles: 128-byte k-rows whose 16-byte chunks are XOR-ed
-// with 4*((k/2)%2).  A transposing fragment read takes 4 consecutive k-rows
-// x 32 bytes per 16 lanes; with the swizzle the 32 lanes of a half-wave hit
-// 8 distinct 32-byte slots of the 256-byte bank window.
-__device__ __forceinline__ int res_lds_off(int kr, int ch) { return kr * 128 + ((ch ^ (((kr >> 1) & 1) << 2)) << 4); }
+// with 4*((k/2 ^ k/8)%2).  A transposing fragment read takes k-rows
+// k0..k0+3 (lanes 0-31) and k0+8..k0+11 (lanes 32-63), 64 bytes each: the
+// k/2 term separates rows k0 and k0+2 within a 256-byte bank window, the k/8
+// term rows k0 and k0+8 within a 512-byte one.
+__device__ __forceinline__ int res_lds_off(int kr, int ch) {
+  return kr * 128 + ((ch ^ ((((kr >> 1) ^ (kr >> 3)) & 1) << 2)) << 4);
+}
 
 // 32 columns (cb .. cb+31) x 16 k of a [k][64] tile: lane -> column cb + lane%32,
 // k = kk*16 + 8*(lane/32) + 0..7 (the K-contiguous fragment layout).
@@ -1458,9 +1461,10 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   OutT* dW = (OutT*)g.out0;
   char* stage = stage_raw + wave * STAGE_WAVE;
   // byte offset of 16-byte chunk c (0..7) of staging row r: chunks XOR-ed
-  // with (r/2)%8, so 16 lanes writing one chunk of 16 rows, or reading two
-  // whole rows, touch 16 distinct bank groups
-  auto stage_off = [](int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); };
+  // with (r/2 ^ r/16)%8, so one chunk of 32 consecutive rows (a half-wave's
+  // write) and whole rows (the reads) spread over distinct 16-byte bank
+  // groups whether banks repeat every 256 or every 512 bytes
+  auto stage_off = [](int r, int c) { return r * 128 + ((c ^ (((r >> 1) ^ (r >> 4)) & 7)) << 4); };
   bf16x8_t bres[2][NKK];
   f32x16 acc[2][2];
   auto row_ptr = [&](int e, int m) -> OutT* {
