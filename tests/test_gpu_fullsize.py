@@ -114,7 +114,8 @@ def halves(x, layout):
 
 
 @pytest.mark.parametrize("name,which", [("gptoss", "coldest"), ("gptoss", "median"), ("backward", "coldest"),
-                                        ("backward", "median"), ("zipf", "coldest"), ("zipf", "median")])
+                                        ("backward", "median"), ("backward", "resident_max"),
+                                        ("backward", "tiled_min"), ("zipf", "coldest"), ("zipf", "median")])
 def test_backward_sampled_experts(name, which):
     check_sampled_expert(run_workload(name), which)
 
@@ -129,7 +130,13 @@ def check_sampled_expert(r, which):
     wl = r["wl"]
     counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
     nonempty = [e for e in np.argsort(counts, kind="stable") if counts[e] > 0]
-    e = {"coldest": nonempty[0], "median": nonempty[len(nonempty) // 2], "hottest": nonempty[-1]}[which]
+    # resident_max / tiled_min: the experts on either side of the resident
+    # weight-gradient kernel's limit of 240 positions (bf16 gradients)
+    below = [x for x in nonempty if counts[x] <= 240]
+    above = [x for x in nonempty if counts[x] > 240]
+    pick = {"coldest": lambda: nonempty[0], "median": lambda: nonempty[len(nonempty) // 2],
+            "hottest": lambda: nonempty[-1], "resident_max": lambda: below[-1], "tiled_min": lambda: above[0]}
+    e = pick[which]()
     slots, Xe, ids1, w1, dYe = expert_subproblem(r, e)
     gu, dn = expert_fetch(r)(e)
     got = {}
