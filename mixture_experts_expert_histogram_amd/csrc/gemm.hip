@@ -918,9 +918,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
 // ---------------------------------------------------------------- weight grads
 // dW[e][m, n] = sum over the expert's positions p of A[p, m] * B[p, n]; both
 // operands are position-major rows (hidden and d_out pre-gathered into
-// expert order), so both are MN-contiguous.  The output (E x M x N fp32,
-// written once) dominates the traffic and the K loops are short (an expert's
-// positions), so the kernel is built around keeping the store stream busy:
+// expert order), so both are MN-contiguous.  This tiled kernel takes the
+// experts above the resident-operand kernel's limit (bf16 gradients) and
+// every expert when gradients are stored in fp32.  The output (E x M x N,
+// written once) dominates the traffic and the K loops can be short (an
+// expert's positions), so the kernel is built around keeping the store
+// stream busy:
 //
 // * One persistent workgroup per CU with two roles.  The MMA waves (C::NT
 //   threads: 8 waves of 64x32 for bf16) load operands and run the MFMAs; four
@@ -1252,27 +1255,29 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 // ------------------------------------------------ weight gradients, resident
 // Experts with at most KMAX positions, bf16 operands and bf16 gradients.  The
 // product dW[e] = A_e^T B_e (M x N) contracts over the expert's c <= KMAX
-// positions, so each dW element carries only 2c flops.  The tiled kernel
-// reloads both operands for every 128 x 128 output tile and stages the tile
-// through LDS.  That moves several times more LDS bytes than the tile writes
-// to HBM.  Here:
-// * A work item is (expert, 128-column block of N).  Each of the 4 MMA waves
-//   (2 x 2, 64 x 64 of the output each) reads its 64 columns of B_e x all c
-//   positions into registers once per item.  This is the resident operand:
-//   up to KMAX/2 bf16 per lane per 32 columns.
-// * The item then sweeps M in 128-row steps.  The A_e tile (c positions x 128
-//   rows of M) is stored in [k][128] rows with the transposing-read swizzle,
-//   in one of two LDS buffers, while the MMA waves multiply the other.  There
-//   is one barrier per tile.
+// positions, so each dW element carries only 2c flops and the kernel's work
+// is mostly writing dW.  The tiled kernel reloads both operands for every
+// 128 x 128 output tile and stages the tile through LDS, which moves several
+// times more LDS bytes than the tile writes to HBM.  Here:
+// * A work item is (expert, 256-column block of N).  Each of the 4 MMA waves
+//   owns 64 of the columns and reads B_e for them x all c positions into
+//   registers once per item: the resident operand, up to KMAX/2 bf16 per
+//   lane per 32 columns.  B_e arrives as four 64-column LDS slices, one per
+//   wave.
+// * The item then sweeps M in 64-row steps.  The A_e tile (c positions x 64
+//   rows of M) is stored as [k][64] rows with a transposing-read swizzle, in
+//   one of two LDS buffers, while the MMA waves multiply the other (64 x 64
+//   of dW per wave).  There is one barrier per tile.
 // * Two groups of two loader waves take alternate tiles.  A group issues a
 //   tile's loads two barrier intervals before the tile is due.  Loaders only
 //   load and MMA waves only store, so neither waits on the other's memory
 //   counter.
-// * The MMA waves round the accumulators to bf16 (v_cvt_pk_bf16_f32), re-tile
-//   each 32 x 64 block through 4 KB of wave-private LDS, and store whole
-//   128-byte row segments.  A store straight from the accumulator layout
-//   touches 32 cache lines per instruction, and the resulting address traffic
-//   held up the operand loads.
+// * The MMA waves round the accumulators to bf16 (v_cvt_pk_bf16_f32), swap
+//   half-rows between the half-waves (v_permlane32_swap) and stage the 64 x 64
+//   block in wave-private LDS (two buffers).  In the next step they store it
+//   as whole 128-byte row segments, non-temporal, one store per k-slice, so
+//   the store stream drains while the matrix cores work.  A store straight
+//   from the accumulator layout touches 32 cache lines per instruction.
 // * An expert without positions gets zeros, written before any operand is
 //   resident.
 // Items of one expert go to one XCD, dealt to its workgroups in order, so the
