@@ -117,10 +117,10 @@ def kernel_model(wl, counts, grad_bytes):
         "gate_up_dgrad": (Wgu + S * 2 * I * eb + S * H * 4, 4.0 * S * H * I),
         "topkw_reduce": (S * 4 * 2, 0.0),
     }
-    # Weight gradients.  With bf16 operands and bf16 gradients, experts with at
-    # most RES_KMAX positions (and those without any) take the resident-operand
-    # kernel, named wgrad_down / wgrad_gate_up, and the rest the tiled kernel,
-    # named *_hot; otherwise the tiled kernel takes every expert under the
+    # Weight gradients.  With bf16 operands, experts with at most RES_KMAX
+    # positions (and those without any) take the resident-operand kernel,
+    # named wgrad_down / wgrad_gate_up, and the rest the tiled kernel, named
+    # *_hot; with fp32 operands the tiled kernel takes every expert under the
     # plain names.  Token-row reads are prorated by the positions each covers.
     def wgrad(sel):
         s_part = int(counts[sel].sum())
@@ -129,7 +129,7 @@ def kernel_model(wl, counts, grad_bytes):
         down = (tok * T * H * eb + s_part * I * eb + e_part * H * I * grad_bytes, 2.0 * s_part * H * I)
         gu = (s_part * 2 * I * eb + tok * T * H * eb + e_part * 2 * I * H * grad_bytes, 4.0 * s_part * H * I)
         return down, gu
-    if wl.dtype == "bf16" and grad_bytes == 2:
+    if wl.dtype == "bf16":
         small = counts <= RES_KMAX
         m["wgrad_down"], m["wgrad_gate_up"] = wgrad(small)
         if (~small).any():

@@ -919,8 +919,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
 // dW[e][m, n] = sum over the expert's positions p of A[p, m] * B[p, n]; both
 // operands are position-major rows (hidden and d_out pre-gathered into
 // expert order), so both are MN-contiguous.  This tiled kernel takes the
-// experts above the resident-operand kernel's limit (bf16 gradients) and
-// every expert when gradients are stored in fp32.  The output (E x M x N,
+// experts above the resident-operand kernel's limit with bf16 operands, and
+// every expert with fp32 operands.  The output (E x M x N,
 // written once) dominates the traffic and the K loops can be short (an
 // expert's positions), so the kernel is built around keeping the store
 // stream busy:
@@ -1253,7 +1253,7 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 }
 
 // ------------------------------------------------ weight gradients, resident
-// Experts with at most KMAX positions, bf16 operands and bf16 gradients.  The
+// Experts with at most KMAX positions, bf16 operands, bf16 or fp32 gradients.  The
 // product dW[e] = A_e^T B_e (M x N) contracts over the expert's c <= KMAX
 // positions, so each dW element carries only 2c flops and the kernel's work
 // is mostly writing dW.  The tiled kernel reloads both operands for every
@@ -1272,12 +1272,14 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
 //   tile's loads two barrier intervals before the tile is due.  Loaders only
 //   load and MMA waves only store, so neither waits on the other's memory
 //   counter.
-// * The MMA waves round the accumulators to bf16 (v_cvt_pk_bf16_f32), swap
-//   half-rows between the half-waves (v_permlane32_swap) and stage the 64 x 64
-//   block in wave-private LDS (two buffers).  In the next step they store it
-//   as whole 128-byte row segments, non-temporal, one store per k-slice, so
-//   the store stream drains while the matrix cores work.  A store straight
-//   from the accumulator layout touches 32 cache lines per instruction.
+// * For bf16 gradients the MMA waves round the accumulators
+//   (v_cvt_pk_bf16_f32), swap half-rows between the half-waves
+//   (v_permlane32_swap) and stage the 64 x 64 block in wave-private LDS (two
+//   buffers); fp32 accumulators are staged as they are (one buffer).  In the
+//   next step they store the block as whole row segments (128 bytes bf16, 256
+//   fp32), non-temporal, one store per k-slice, so the store stream drains
+//   while the matrix cores work.  A store straight from the accumulator layout
+//   touches 32 cache lines per instruction.
 // * An expert without positions gets zeros, written before any operand is
 //   resident.
 // Items of one expert go to one XCD, dealt to its workgroups in order, so the
@@ -1358,16 +1360,21 @@ __device__ __forceinline__ bf16x8_t frag_k64(const char* tile, int cb, int kk, i
   return out;
 }
 
-template <bool GATE_UP, int KMAX>
+// OutT: bf16 (uint16_t) or fp32 gradients.
+template <bool GATE_UP, typename OutT, int KMAX>
 __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
-  using OutT = uint16_t;   // bf16 gradients
+  constexpr bool BF = sizeof(OutT) == 2;
   constexpr int NKK = KMAX / 16;
   constexpr int TILE_BYTES = KMAX * kResM * 2;
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * TILE_BYTES];
   __shared__ WgradTables tab;
-  // per MMA wave, two buffers of 64 rows x 128 bytes to re-tile a step's
-  // 64 x 64 accumulator block into whole 128-byte row segments
-  constexpr int STAGE_BUF = 64 * 128, STAGE_WAVE = 2 * STAGE_BUF;
+  // Per MMA wave, the staging rows that re-tile a step's 64 x 64 accumulator
+  // block into whole row segments: two buffers of 64 rows x 128 bytes for
+  // bf16, one of 64 x 256 bytes for fp32.  One buffer suffices because a
+  // block's stores are all issued before the next block is staged; the bf16
+  // path keeps its measured two-buffer form.
+  constexpr int SROW = 64 * (int)sizeof(OutT), CPRS = SROW / 16;   // bytes, chunks per staged row
+  constexpr int STAGE_BUF = 64 * SROW, STAGE_WAVE = BF ? 2 * STAGE_BUF : STAGE_BUF;
   __shared__ __attribute__((aligned(16))) char stage_raw[4 * STAGE_WAVE];
   const int H = g.H, I = g.I;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
@@ -1465,11 +1472,15 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   const int lane = threadIdx.x & 63;
   OutT* dW = (OutT*)g.out0;
   char* stage = stage_raw + wave * STAGE_WAVE;
-  // byte offset of 16-byte chunk c (0..7) of staging row r: chunks XOR-ed
-  // with (r/2 ^ r/16)%8, so one chunk of 32 consecutive rows (a half-wave's
-  // write) and whole rows (the reads) spread over distinct 16-byte bank
-  // groups whether banks repeat every 256 or every 512 bytes
-  auto stage_off = [](int r, int c) { return r * 128 + ((c ^ (((r >> 1) ^ (r >> 4)) & 7)) << 4); };
+  // byte offset of 16-byte chunk c of staging row r: chunks XOR-ed with
+  // (r/2 ^ r/16)%8 for 128-byte rows, (r ^ r/16)%16 for 256-byte rows, so one
+  // chunk of 32 consecutive rows (a half-wave's write) and whole rows (the
+  // reads) spread over distinct 16-byte bank groups whether banks repeat
+  // every 256 or every 512 bytes
+  auto stage_off = [](int r, int c) {
+    if constexpr (BF) return r * 128 + ((c ^ (((r >> 1) ^ (r >> 4)) & 7)) << 4);
+    else return r * 256 + ((c ^ ((r ^ (r >> 4)) & 15)) << 4);
+  };
   bf16x8_t bres[2][NKK];
   f32x16 acc[2][2];
   auto row_ptr = [&](int e, int m) -> OutT* {
@@ -1490,36 +1501,50 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn) {
-        // Register groups 2p and 2p+1 hold columns 16p + 4h + 0..3 and
-        // 16p + 8 + 4h + 0..3 (h = lane / 32).  Swapping group 2p+1 of the
-        // lower half-wave with group 2p of the upper one gives lane h 8
-        // consecutive columns 16p + 8h + 0..7 (16-byte chunk 4fn + 2p + h
-        // of the row).
+        const f32x16& a = acc[fm][fn];
+        const int r = fm * 32 + (lane & 31);
+        if constexpr (BF) {
+          // Register groups 2p and 2p+1 hold columns 16p + 4h + 0..3 and
+          // 16p + 8 + 4h + 0..3 (h = lane / 32).  Swapping group 2p+1 of the
+          // lower half-wave with group 2p of the upper one gives lane h 8
+          // consecutive columns 16p + 8h + 0..7 (16-byte chunk 4fn + 2p + h
+          // of the row).
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const f32x16& a = acc[fm][fn];
-          const uint32_t p0 = pack_bf16(a[8 * p], a[8 * p + 1]);
-          const uint32_t p1 = pack_bf16(a[8 * p + 2], a[8 * p + 3]);
-          const uint32_t q0 = pack_bf16(a[8 * p + 4], a[8 * p + 5]);
-          const uint32_t q1 = pack_bf16(a[8 * p + 6], a[8 * p + 7]);
-          const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
-          const int r = fm * 32 + (lane & 31), c = 4 * fn + 2 * p + (lane >> 5);
-          *(uint4*)(st + stage_off(r, c)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          for (int p = 0; p < 2; ++p) {
+            const uint32_t p0 = pack_bf16(a[8 * p], a[8 * p + 1]);
+            const uint32_t p1 = pack_bf16(a[8 * p + 2], a[8 * p + 3]);
+            const uint32_t q0 = pack_bf16(a[8 * p + 4], a[8 * p + 5]);
+            const uint32_t q1 = pack_bf16(a[8 * p + 6], a[8 * p + 7]);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+            const int c = 4 * fn + 2 * p + (lane >> 5);
+            *(uint4*)(st + stage_off(r, c)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          }
+        } else {
+          // register group vg: columns 8vg + 4h + 0..3, chunk 8fn + 2vg + h
+#pragma unroll
+          for (int vg = 0; vg < 4; ++vg) {
+            const int c = 8 * fn + 2 * vg + (lane >> 5);
+            *(float4*)(st + stage_off(r, c)) = make_float4(a[4 * vg], a[4 * vg + 1], a[4 * vg + 2], a[4 * vg + 3]);
+          }
         }
       }
   };
+
   // Pending staged block: rows pj*64.., columns pn0 + wave*64.. of expert pe.
   int pe = 0, pj = 0, pn0 = 0;
   bool pending = false;
   const char* pst = stage;
-  // Store q (0..7) of the pending block: staged rows 8q .. 8q+7, 8 lanes per
-  // row, one whole 128-byte row segment each, non-temporal (dW is not read
-  // again here, so it need not displace the operand tiles in L2).
+  // Store q (0..NQ-1) of the pending block: RPI staged rows, CPRS lanes per
+  // row, one whole row segment (128 bytes bf16, 256 fp32) each, non-temporal
+  // (dW is not read again here, so it need not displace the operand tiles in
+  // L2).
+  constexpr int RPI = 64 / CPRS, NQ = 64 / RPI, VPC = 16 / (int)sizeof(OutT);
+  constexpr int NQI = NQ < 8 ? NQ : 8;   // stores issued between k-slices; the rest after them
   auto store_step = [&](int q) {
-    const int r = q * 8 + (lane >> 3), c = lane & 7;
+    const int r = q * RPI + lane / CPRS, c = lane % CPRS;
     const uint4 v = *(const uint4*)(pst + stage_off(r, c));
-    const int m = pj * kResM + r, n = pn0 + wave * 64 + c * 8;
+    const int m = pj * kResM + r, n = pn0 + wave * 64 + c * VPC;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     if (m < M && n < N) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)(row_ptr(pe, m) + n));
   };
@@ -1528,8 +1553,8 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   for (int i = w0; i < list.count; i += list.K) {
     const ResItem it = list.item(i);
     if (it.cnt != 0) continue;
-    constexpr int CPR = kResN / 8;   // 16-byte chunks per row of the item
-    const int c = (threadIdx.x % CPR) * 8;
+    constexpr int VPC0 = 16 / (int)sizeof(OutT), CPR = kResN / VPC0;   // 16-byte chunks per row of the item
+    const int c = (threadIdx.x % CPR) * VPC0;
     if (c < N - it.n0)
       for (int m = threadIdx.x / CPR; m < M; m += 256 / CPR)
         *(uint4*)(row_ptr(it.e, m) + it.n0 + c) = make_uint4(0u, 0u, 0u, 0u);
@@ -1570,13 +1595,13 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
             for (int fn = 0; fn < 2; ++fn)
               acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bres[fn][kk], a[kk & 1][fm],
                                                                      kk == 0 ? f32x16{} : acc[fm][fn], 0, 0, 0);
-          if (kk < 8 && pending) store_step(kk);
+          if (kk < NQI && pending) store_step(kk);
         }
       }
       if (pending)
-        for (int q = it.nkk; q < 8; ++q) store_step(q);
-      // stage this step's block in the other buffer; it is stored during the next step
-      char* st = stage + (pst == stage ? STAGE_BUF : 0);
+        for (int q = min(it.nkk, NQI); q < NQ; ++q) store_step(q);
+      // stage this step's block (bf16: in the other buffer); it is stored during the next step
+      char* st = stage + (BF && pst == stage ? STAGE_BUF : 0);
       stage_acc(st);
       pst = st;
       pe = it.e;
@@ -1586,7 +1611,7 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
     }
   }
   if (pending)
-    for (int q = 0; q < 8; ++q) store_step(q);
+    for (int q = 0; q < NQ; ++q) store_step(q);
 }
 
 // ------------------------------------------------------------------ host side
@@ -1788,28 +1813,28 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
 // Experts with at most this many positions take the resident-operand kernel.
 constexpr int kResKmax = 240;
 
-template <bool GU>
+template <bool GU, typename OutT>
 static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
   GArgs g = base_args(pb, 128);
   g.A = A; g.B = B; g.out0 = dW;
-  if (GU) set_gu(g, pb, nullptr, dW, 2);
+  if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
   static const int cus = device_cus();
   const long grid = (cus / 8) * 8;
   return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s, [&] {
-    wgrad_res_kernel<GU, kResKmax><<<grid, kResThreads, 0, s>>>(g);
+    wgrad_res_kernel<GU, OutT, kResKmax><<<grid, kResThreads, 0, s>>>(g);
   });
 }
 
 template <bool GU>
 static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
-  if (pb.dtype == 0 && pb.gdtype == 0 && pb.S > 0) {
-    // bf16 gradients: experts with at most kResKmax positions (and those
-    // without any), then the rest.  fp32 gradients stay on the tiled kernel,
-    // whose staged whole-row stores write them faster than the accumulator
-    // layout does.
-    const hipError_t e = wgrad_res_impl<GU>(pb, A, B, dW, s);
+  if (pb.dtype == 0 && pb.S > 0) {
+    // bf16 operands: experts with at most kResKmax positions (and those
+    // without any) on the resident-operand kernel, then the rest
+    const hipError_t e = pb.gdtype == 0 ? wgrad_res_impl<GU, uint16_t>(pb, A, B, dW, s)
+                                        : wgrad_res_impl<GU, float>(pb, A, B, dW, s);
     if (e != hipSuccess) return e;
-    return wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax);
+    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax)
+                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax);
   }
   if (pb.dtype == 0)
     return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, -1)

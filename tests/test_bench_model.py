@@ -1,10 +1,11 @@
 """The benchmark's roofline model of one launch per kernel (host logic, CPU).
 
-With bf16 operands and bf16 gradients the weight gradients run as two
-kernels: the resident-operand one for experts of at most RES_KMAX positions
-(and empty experts) and the tiled one for the rest.  The two model entries
-must split the useful flops and the gradient bytes by expert exactly; with
-fp32 gradients a single entry covers every expert.
+With bf16 operands the weight gradients run as two kernels: the
+resident-operand one for experts of at most RES_KMAX positions (and empty
+experts) and the tiled one for the rest, whether the gradients are stored in
+bf16 or fp32.  The two model entries must split the useful flops and the
+gradient bytes by expert exactly; with fp32 operands a single entry covers
+every expert.
 """
 import numpy as np
 import pytest
@@ -29,12 +30,9 @@ def test_weight_gradient_split_covers_every_expert(grad_bytes):
     for name, per_flop in [("wgrad_down", 2.0), ("wgrad_gate_up", 4.0)]:
         parts = [m[name]] + ([m[name + "_hot"]] if name + "_hot" in m else [])
         assert sum(p[1] for p in parts) == pytest.approx(per_flop * S * H * I)
-        if grad_bytes == 2:
-            small = counts <= bench.RES_KMAX
-            assert m[name][1] == pytest.approx(per_flop * counts[small].sum() * H * I)
-            assert m[name + "_hot"][1] == pytest.approx(per_flop * counts[~small].sum() * H * I)
-        else:
-            assert name + "_hot" not in m
+        small = counts <= bench.RES_KMAX
+        assert m[name][1] == pytest.approx(per_flop * counts[small].sum() * H * I)
+        assert m[name + "_hot"][1] == pytest.approx(per_flop * counts[~small].sum() * H * I)
         # every expert's gradient is written once, by exactly one of the kernels,
         # and the operand rows are read once in total
         dw = (2 if name == "wgrad_gate_up" else 1) * E * H * I * grad_bytes
@@ -47,3 +45,10 @@ def test_no_hot_entry_without_hot_experts():
     counts = np.full(wl.E, wl.S // wl.E, dtype=np.int64)
     m = bench.kernel_model(wl, counts, 2)
     assert "wgrad_gate_up_hot" not in m and "wgrad_down_hot" not in m
+
+
+def test_fp32_operands_use_one_entry():
+    wl = Workload("model32", 600, 64, 32, 4, 1, "fp32", "swiglu", "concat")
+    counts = np.array([300, 250, 50, 0])
+    m = bench.kernel_model(wl, counts, 4)
+    assert "wgrad_gate_up_hot" not in m and m["wgrad_gate_up"][1] == pytest.approx(4.0 * 600 * 64 * 32)
