@@ -814,30 +814,47 @@ __global__ __launch_bounds__(C::NT, C::OCC) void down_dgrad_kernel(GArgs g) {
   T* aw = (T*)g.out1;
   const int layout = g.layout;
   float* red = (float*)smem_raw;   // [WN][BM]; the K loop ended with a barrier
+  // Per 32-row group, all of the lane's Z values are loaded first, from
+  // addresses clamped into the tile (rows past the tile's end read its last
+  // row, columns past I the last four), and only the results are
+  // predicated.  Loads issued one register group at a time behind the bounds
+  // test each waited out the HBM latency: 0.84 -> 0.78 ms on the gpt-oss
+  // layer, 4.60 -> 4.00 ms on the Zipf batch.
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int rl = wm * C::WTM + fm * 32 + (lane & 31);
     float rs = 0.f;
+    const size_t p = (size_t)(m0 + min(rl, rows - 1));
+    const float w = g.w_of_pos[p];
+    const float* zr = Z + p * 2 * I;
+    T* dzr = dZ + p * 2 * I;
+    // interleaved rows: (g, u) pairs, za = columns i, i+1, zb = i+2, i+3;
+    // concatenated rows: za = gate, zb = up, columns i .. i+3
+    float4 za[C::FN][4], zb[C::FN][4];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int i = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+        const int ic = i < I ? i : I - 4;   // I is a multiple of 8
+        za[fn][vg] = *(const float4*)(zr + (layout ? 2 * ic : ic));
+        zb[fn][vg] = *(const float4*)(zr + (layout ? 2 * ic + 4 : I + ic));
+      }
     if (rl < rows) {
-      const size_t p = (size_t)(m0 + rl);
-      const float w = g.w_of_pos[p];
-      const float* zr = Z + p * 2 * I;
-      T* dzr = dZ + p * 2 * I;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
         for (int vg = 0; vg < 4; ++vg) {
           const int i = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
           if (i >= I) continue;
+          const float4 z0 = za[fn][vg], z1 = zb[fn][vg];
           float gv[4], uv[4];
           if (layout) {
-            const float4 z0 = *(const float4*)(zr + 2 * i), z1 = *(const float4*)(zr + 2 * i + 4);
             gv[0] = z0.x; uv[0] = z0.y; gv[1] = z0.z; uv[1] = z0.w;
             gv[2] = z1.x; uv[2] = z1.y; gv[3] = z1.z; uv[3] = z1.w;
           } else {
-            const float4 zg = *(const float4*)(zr + i), zu = *(const float4*)(zr + I + i);
-            gv[0] = zg.x; gv[1] = zg.y; gv[2] = zg.z; gv[3] = zg.w;
-            uv[0] = zu.x; uv[1] = zu.y; uv[2] = zu.z; uv[3] = zu.w;
+            gv[0] = z0.x; gv[1] = z0.y; gv[2] = z0.z; gv[3] = z0.w;
+            uv[0] = z1.x; uv[1] = z1.y; uv[2] = z1.z; uv[3] = z1.w;
           }
           float dg[4], du[4], a[4];
 #pragma unroll
@@ -1729,7 +1746,7 @@ hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, voi
   return use_bm192(pb) ? down_impl<CfgB192>(pb, a, Wd, Yp, s) : down_impl<CfgB>(pb, a, Wd, Yp, s);
 }
 
-int down_dgrad_nparts(int I) { return (I + 127) / 128; }   // both configs use BN = 128
+int down_dgrad_nparts(int I) { return (I + 127) / 128; }   // every down dgrad config uses BN = 128
 
 template <class C>
 static hipError_t down_dgrad_impl(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ,
@@ -1746,10 +1763,12 @@ hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* 
                              void* aw, float* partials, int* nparts, hipStream_t s) {
   *nparts = down_dgrad_nparts(pb.I);
   if (pb.S == 0) return hipSuccess;
-  // (192-row tiles measured no faster here: its GLU-backward epilogue leaves
-  // room for only one register set of prefetch at that height)
-  return pb.dtype == 0 ? down_dgrad_impl<CfgB>(pb, dY, Wd, Z, dZ, aw, partials, s)
-                       : down_dgrad_impl<CfgF>(pb, dY, Wd, Z, dZ, aw, partials, s);
+  // 192-row tiles when experts average 101-176 positions (gpt-oss layer
+  // 0.78 -> 0.71 ms); 256-row tiles for larger experts measured slower here
+  // (Zipf batch 3.99 -> 4.04 ms), so those keep 128 rows.
+  if (pb.dtype != 0) return down_dgrad_impl<CfgF>(pb, dY, Wd, Z, dZ, aw, partials, s);
+  return use_bm192(pb) ? down_dgrad_impl<CfgB192>(pb, dY, Wd, Z, dZ, aw, partials, s)
+                       : down_dgrad_impl<CfgB>(pb, dY, Wd, Z, dZ, aw, partials, s);
 }
 
 template <class C>
