@@ -98,6 +98,7 @@ def measured_traffic(kernel, workload, grad_dtype):
 
 # ------------------------------------------------------------------ per-kernel model
 RES_KMAX = 240   # the resident-operand weight gradient's limit (positions per expert)
+LONG_MIN = 1024  # experts with more positions take the long-K weight gradient
 def kernel_model(wl, counts, grad_bytes):
     """Algorithmic bytes and flops of one launch of each kernel.
 
@@ -119,9 +120,10 @@ def kernel_model(wl, counts, grad_bytes):
     }
     # Weight gradients.  With bf16 operands, experts with at most RES_KMAX
     # positions (and those without any) take the resident-operand kernel,
-    # named wgrad_down / wgrad_gate_up, and the rest the tiled kernel, named
-    # *_hot; with fp32 operands the tiled kernel takes every expert under the
-    # plain names.  Token-row reads are prorated by the positions each covers.
+    # named wgrad_down / wgrad_gate_up, those with more than LONG_MIN the
+    # long-K kernel (*_long) and the rest the tiled kernel (*_hot); with fp32
+    # operands the tiled kernel takes every expert under the plain names.
+    # Token-row reads are prorated by the positions each covers.
     def wgrad(sel):
         s_part = int(counts[sel].sum())
         e_part = int(sel.sum())
@@ -131,9 +133,13 @@ def kernel_model(wl, counts, grad_bytes):
         return down, gu
     if wl.dtype == "bf16":
         small = counts <= RES_KMAX
+        long_ = counts > LONG_MIN
+        mid = ~small & ~long_
         m["wgrad_down"], m["wgrad_gate_up"] = wgrad(small)
-        if (~small).any():
-            m["wgrad_down_hot"], m["wgrad_gate_up_hot"] = wgrad(~small)
+        if mid.any():
+            m["wgrad_down_hot"], m["wgrad_gate_up_hot"] = wgrad(mid)
+        if long_.any():
+            m["wgrad_down_long"], m["wgrad_gate_up_long"] = wgrad(long_)
     else:
         m["wgrad_down"], m["wgrad_gate_up"] = wgrad(counts >= 0)
     return m

@@ -575,6 +575,7 @@ struct GArgs {
   int ntn, ntm, nparts;
   int big;   // weight grads: experts with more positions than this are split over the XCDs
   int small_max;   // weight grads: the tiled kernel takes only experts with more positions (-1: all)
+  int hot_min;     // weight grads: experts with more positions go to the long-K kernel (0: none)
   // Gate/up rows of the weights (gu_*) and of their gradients (dgu_*): row j of
   // expert e's gate (up) projection starts gu_es*e + gu_rs*j elements after
   // gu_g (gu_u).  Fused [E,2I,H] concatenated: (W, W + I*H, 2IH, H);
@@ -646,11 +647,11 @@ __device__ __forceinline__ bool row_tile(const GArgs& g, int& e, int& m0, int& r
 }
 
 // Weight-gradient tiles: chunks of 8 consecutive tiles are dealt round-robin
-// to the XCDs in launch order (experts longest first), so every XCD gets a
-// similar share of long and short experts and a chunk's tiles share operands
-// in one L2.  Returns -1 past the end.
-__device__ __forceinline__ int dealt_tile(int total) {
-  const int b = blockIdx.x, x = b & 7, j = b >> 3;
+// to the XCDs (experts longest first), so every XCD gets a similar share of
+// long and short experts and a chunk's tiles share operands in one L2.  The
+// j-th tile of this workgroup's XCD, or -1 past the end.
+__device__ __forceinline__ int dealt_tile(int j, int total) {
+  const int x = blockIdx.x & 7;
   const int t = (((j >> 3) << 3) + x) * 8 + (j & 7);
   return t < total ? t : -1;
 }
@@ -991,31 +992,29 @@ struct WgradTables {
 template <class C>
 struct WgradList {
   const WgradTables* tab;   // in LDS
-  int E, ntn, tiles, tpx, nb, x, len_x, count;
+  int E, ntn, tiles, tpx, nb, x, len_x, count, base;
 
+  // number of leading experts (descending count) with more than lim positions
+  __device__ __forceinline__ int leading_above(int lim, int l, int h) const {
+    while (l < h) {
+      const int mid = (l + h) >> 1;
+      const int e = tab->order[mid];
+      if (tab->offsets[e + 1] - tab->offsets[e] > lim) l = mid + 1; else h = mid;
+    }
+    return l;
+  }
   __device__ __forceinline__ void init(const GArgs& g, const WgradTables* t) {
     tab = t;
-    E = g.E;
     ntn = g.ntn;
     const WgradPlan p = wgrad_plan(g.ntm, g.ntn);
     tiles = p.tiles;
     tpx = p.tpx;
-    if (g.small_max >= 0) {   // only the leading experts with more than small_max positions
-      int l = 0, h = E;
-      while (l < h) {
-        const int mid = (l + h) >> 1;
-        const int e = tab->order[mid];
-        if (tab->offsets[e + 1] - tab->offsets[e] > g.small_max) l = mid + 1; else h = mid;
-      }
-      E = l;
-    }
-    int l = 0, h = E;   // nb = leading experts (descending count) with count > big
-    while (l < h) {
-      const int mid = (l + h) >> 1;
-      const int e = tab->order[mid];
-      if (tab->offsets[e + 1] - tab->offsets[e] > g.big) l = mid + 1; else h = mid;
-    }
-    nb = l;
+    // the list is order[base .. hi): experts above hot_min are the long-K
+    // kernel's, those at or below small_max the resident kernel's
+    const int hi = g.small_max >= 0 ? leading_above(g.small_max, 0, g.E) : g.E;
+    base = g.hot_min > 0 ? min(leading_above(g.hot_min, 0, g.E), hi) : 0;
+    E = hi - base;
+    nb = leading_above(g.big, base, hi) - base;   // experts with count > big, split over the XCDs
     x = blockIdx.x & 7;
     len_x = max(0, min((x + 1) * tpx, tiles) - x * tpx);
     const int npin = E - nb - x > 0 ? (E - nb - x + 7) / 8 : 0;
@@ -1036,7 +1035,7 @@ struct WgradList {
       er = nb + x + 8 * q;
     }
     WItem it;
-    it.e = tab->order[er];
+    it.e = tab->order[base + er];
     it.off = tab->offsets[it.e];
     it.cnt = tab->offsets[it.e + 1] - it.off;
     if (it.cnt == 0) it.off = 0;
@@ -1631,6 +1630,91 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
     for (int q = 0; q < NQ; ++q) store_step(q);
 }
 
+// ------------------------------------------------ weight gradients, long K
+// Experts with more than hot_min positions (bf16 operands).  Their K loop
+// (the expert's positions) runs to thousands, so dW[e] = A_e^T B_e is a plain
+// long-K GEMM whose stores are a small share of the time: 128 x 128 tiles on
+// the token-row engine's two-set pipeline (two workgroups per CU), both
+// operands position-major in [k][128] LDS tiles read with transposing LDS
+// reads.  A persistent grid deals chunks of 8 tiles round-robin to the XCDs,
+// so each XCD gets a share of every expert (one hot expert can hold a fifth
+// of all positions; contiguous ranges per XCD left one XCD with a third of
+// the work, 2x slower).  Inside an expert, groups of 8 M-tiles run N-tile by
+// N-tile, so a chunk's 8 tiles share their B row block and an XCD's chunks
+// of one group share the A row blocks in its L2.  The tiled kernel, built
+// around short K loops and the dW store stream, took these experts at ~550
+// TFLOP/s.
+template <class C, bool GATE_UP, typename OutT>
+__global__ __launch_bounds__(C::NT, C::OCC) void wgrad_long_kernel(GArgs g) {
+  GEMM_PROLOGUE(C)
+  static_assert(C::BM == 128 && C::BN == 128, "[k][128] operand tiles");
+  const int I = g.I, H = g.H;
+  const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
+  const int lda = M, ldb = N;   // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
+  int l = 0, h = g.E;           // nhot = leading experts with more than hot_min positions
+  while (l < h) {
+    const int mid = (l + h) >> 1;
+    const int e = g.expert_order[mid];
+    if (g.offsets[e + 1] - g.offsets[e] > g.hot_min) l = mid + 1; else h = mid;
+  }
+  const int ntm = g.ntm, ntn = g.ntn, per_e = ntm * ntn;
+  const int total = l * per_e;
+  const int K = gridDim.x >> 3;
+  const T* Ag = (const T*)g.A;
+  const T* Bg = (const T*)g.B;
+  OutT* dW = (OutT*)g.out0;
+  // this XCD's j-th tile: chunks of 8 consecutive tiles dealt round-robin to
+  // the XCDs (increasing in j, so the first one past the end ends the loop)
+  for (int j = blockIdx.x >> 3;; j += K) {
+    const int t = dealt_tile(j, total);
+    if (t < 0) break;
+    const int er = t / per_e, local = t - er * per_e;
+    const int e = g.expert_order[er];
+    const int off = g.offsets[e], cnt = g.offsets[e + 1] - off;   // cnt > hot_min > 0
+    const int gsz = kRowTileGroup * ntn;
+    const int grp = local / gsz, rem = local - grp * gsz;
+    const int gm = min(kRowTileGroup, ntm - grp * kRowTileGroup);
+    const int nt = rem / gm, mt = grp * kRowTileGroup + (rem - nt * gm);
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    NLoader<C, 0> al;
+    NLoader<C, C::NT / 2> bl;
+    al.init(M - m0, cnt);
+    bl.init(N - n0, cnt);
+    const T* Ap = Ag + (size_t)off * lda + m0;
+    const T* Bp = Bg + (size_t)off * ldb + n0;
+    auto aload = [&](auto& ld, int kt, auto set) {
+      ld.template load<decltype(set)::value>(kt, [&](int k) { return Ap + (size_t)k * lda; });
+    };
+    auto bload = [&](auto& ld, int kt, auto set) {
+      ld.template load<decltype(set)::value>(kt, [&](int k) { return Bp + (size_t)k * ldb; });
+    };
+    f32x16 acc[C::FM][C::FN];
+    mainloop<C, true, true>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
+      if (m >= M) continue;
+      OutT* row;
+      if (GATE_UP && g.gu_sep) {   // separate dW_gate, dW_up: row m is a dZ column
+        int up, jj;
+        zcol(m, I, g.layout, up, jj);
+        row = gu_row((OutT*)g.dgu_g, (OutT*)g.dgu_u, g.gu_es, g.gu_rs, e, up, jj);
+      } else {
+        row = dW + ((size_t)e * M + m) * N;
+      }
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+          if (n < N)
+            store4<OutT>(row + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
+                         acc[fm][fn][vg * 4 + 3]);
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 using CfgB = Cfg<uint16_t, 128, 128, 64, 2, 2>;   // bf16
 // bf16 with 192-row M-tiles (96 rows per wave): when experts average a little
@@ -1803,7 +1887,7 @@ static int device_cus() {
 
 template <class C, bool GU, typename OutT>
 static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s,
-                             int small_max) {
+                             int small_max, int hot_min = 0) {
   const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
   if (pb.S == 0) {   // no positions
     if (GU && pb.dw_up) {
@@ -1821,6 +1905,7 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
   const long mean = ((long)pb.S + pb.E - 1) / pb.E;
   g.big = (int)std::max<long>(2 * mean, 4 * C::BK);
   g.small_max = small_max;
+  g.hot_min = hot_min;
   // one persistent workgroup per CU, a whole number per XCD
   static const int cus = device_cus();
   const long grid = (cus / 8) * 8;
@@ -1844,6 +1929,26 @@ static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const voi
   });
 }
 
+// Experts with more than kLongMin positions take the long-K kernel.
+constexpr int kLongMin = 1024;
+
+template <bool GU, typename OutT>
+static hipError_t wgrad_long_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
+  using C = CfgB;
+  const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
+  GArgs g = base_args(pb, C::BM);
+  g.A = A; g.B = B; g.out0 = dW;
+  if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
+  g.ntm = (M + C::BM - 1) / C::BM;
+  g.ntn = (N + C::BN - 1) / C::BN;
+  g.hot_min = kLongMin;
+  // persistent: C::OCC workgroups per CU, a whole number per XCD
+  static const int cus = device_cus();
+  const long grid = (cus / 8) * 8 * C::OCC;
+  return run_kernel(GU ? "wgrad_gate_up_long" : "wgrad_down_long", s,
+                    [&] { wgrad_long_kernel<C, GU, OutT><<<grid, C::NT, 0, s>>>(g); });
+}
+
 template <bool GU>
 static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
   if (pb.dtype == 0 && pb.S > 0) {
@@ -1852,8 +1957,11 @@ static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const voi
     const hipError_t e = pb.gdtype == 0 ? wgrad_res_impl<GU, uint16_t>(pb, A, B, dW, s)
                                         : wgrad_res_impl<GU, float>(pb, A, B, dW, s);
     if (e != hipSuccess) return e;
-    return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax)
-                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax);
+    const hipError_t e2 = pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax, kLongMin)
+                                         : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax, kLongMin);
+    if (e2 != hipSuccess) return e2;
+    return pb.gdtype == 0 ? wgrad_long_impl<GU, uint16_t>(pb, A, B, dW, s)
+                          : wgrad_long_impl<GU, float>(pb, A, B, dW, s);
   }
   if (pb.dtype == 0)
     return pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, -1)

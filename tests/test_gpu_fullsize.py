@@ -115,7 +115,8 @@ def halves(x, layout):
 
 @pytest.mark.parametrize("name,which", [("gptoss", "coldest"), ("gptoss", "median"), ("backward", "coldest"),
                                         ("backward", "median"), ("backward", "resident_max"),
-                                        ("backward", "tiled_min"), ("zipf", "coldest"), ("zipf", "median")])
+                                        ("backward", "tiled_min"), ("zipf", "coldest"), ("zipf", "median"),
+                                        ("zipf", "long_min")])
 def test_backward_sampled_experts(name, which):
     check_sampled_expert(run_workload(name), which)
 
@@ -131,11 +132,14 @@ def check_sampled_expert(r, which):
     counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
     nonempty = [e for e in np.argsort(counts, kind="stable") if counts[e] > 0]
     # resident_max / tiled_min: the experts on either side of the resident
-    # weight-gradient kernel's limit of 240 positions (bf16 gradients)
+    # weight-gradient kernel's limit of 240 positions; long_min: the smallest
+    # expert above the long-K kernel's threshold of 1024 positions
     below = [x for x in nonempty if counts[x] <= 240]
     above = [x for x in nonempty if counts[x] > 240]
+    long_ = [x for x in nonempty if counts[x] > 1024]
     pick = {"coldest": lambda: nonempty[0], "median": lambda: nonempty[len(nonempty) // 2],
-            "hottest": lambda: nonempty[-1], "resident_max": lambda: below[-1], "tiled_min": lambda: above[0]}
+            "hottest": lambda: nonempty[-1], "resident_max": lambda: below[-1], "tiled_min": lambda: above[0],
+            "long_min": lambda: long_[0]}
     e = pick[which]()
     slots, Xe, ids1, w1, dYe = expert_subproblem(r, e)
     gu, dn = expert_fetch(r)(e)
