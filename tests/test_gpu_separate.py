@@ -31,6 +31,26 @@ def split_weights(wgu, layout):
 def test_separate_weights_match_oracle(act, layout, dtype, grad_dtype, save):
     T, H, I, E, K = 300, 328, 200, 6, 3
     inp = small_inputs(T, H, I, E, K, dtype, act, layout, seed=13, ids=skewed_ids(T, K, E, 13))
+    check_separate(inp, act, layout, dtype, grad_dtype, save)
+
+
+@pytest.mark.parametrize("layout", ["concat", "interleaved"])
+@pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
+def test_separate_weights_all_weight_gradient_kernels(layout, grad_dtype):
+    """Experts of 0, 16, 240, 241, 300, 1025 and 1601 slots: the resident,
+    tiled and long-K weight gradients each write rows of the separate gate
+    and up tensors (tiles straddling their boundary at I = 200)."""
+    counts = [1601, 1025, 300, 241, 240, 16, 0]
+    E, K = len(counts), 1
+    T, H, I = sum(counts), 264, 200
+    rng = np.random.default_rng(41)
+    ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
+    inp = small_inputs(T, H, I, E, K, "bf16", "swiglu", layout, seed=41, ids=ids)
+    check_separate(inp, "swiglu", layout, "bf16", grad_dtype, True)
+
+
+def check_separate(inp, act, layout, dtype, grad_dtype, save):
+    E = inp.wl.E
     d = device_inputs(inp)
     wg, wu = split_weights(d["w_gate_up"], layout)
     kw = dict(act=act, limit=inp.wl.limit, alpha=inp.wl.alpha)
