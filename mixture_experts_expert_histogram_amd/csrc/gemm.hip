@@ -330,8 +330,16 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 // 32 columns x 16 k of an NLoader tile: lane -> column cb + lane%32,
 // k = kk*16 + 8*(lane/32) + 0..7 (the layout of the K-contiguous fragments).
+// Configs whose MN-contiguous A tile is 256 columns wide, held as two
+// [k][128] halves (see the long-K weight gradient).
+template <class C> struct WideA { static constexpr bool value = false; };
+
 template <class C>
 __device__ __forceinline__ bf16x8_t frag_n(const typename C::elem* tile, int cb, int kk, int lane) {
+  if constexpr (WideA<C>::value) {   // columns 128.. live in the second [k][128] half
+    tile += (cb >> 7) * 128 * C::BK;
+    cb &= 127;
+  }
   const int g = lane >> 4, s = lane & 15;
   const int col = cb + ((g & 1) << 4) + ((s & 3) << 2);
   const int chunk = col >> 3, within = (col & 7) * 2;
@@ -1633,10 +1641,11 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
 // ------------------------------------------------ weight gradients, long K
 // Experts with more than hot_min positions (bf16 operands).  Their K loop
 // (the expert's positions) runs to thousands, so dW[e] = A_e^T B_e is a plain
-// long-K GEMM whose stores are a small share of the time: 128 x 128 tiles on
-// the token-row engine's pipeline (two workgroups per CU), both
-// operands position-major in [k][128] LDS tiles read with transposing LDS
-// reads.  A persistent grid deals chunks of 8 tiles round-robin to the XCDs,
+// long-K GEMM whose stores are a small share of the time: 256 x 128 tiles on
+// the token-row engine's two-set pipeline (8 waves of 64 x 64, one workgroup
+// per CU), both operands position-major and read with transposing LDS reads
+// (B as one [k][128] tile, A as two; 128 x 128 tiles at two workgroups per
+// CU were 6 % slower).  A persistent grid deals chunks of 8 tiles round-robin to the XCDs,
 // so each XCD gets a share of every expert (one hot expert can hold a fifth
 // of all positions; contiguous ranges per XCD left one XCD with a third of
 // the work, 2x slower).  Inside an expert, groups of 8 M-tiles run N-tile by
@@ -1644,10 +1653,34 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
 // of one group share the A row blocks in its L2.  The tiled kernel, built
 // around short K loops and the dW store stream, took these experts at ~550
 // TFLOP/s.
+// 256 x 128 tiles on 8 waves (64 x 64 each), one workgroup per CU; the A
+// tile (256 columns of M) is two [k][128] halves.
+struct CfgL : Cfg<uint16_t, 256, 128, 64, 4, 2> {};
+template <> struct WideA<CfgL> { static constexpr bool value = true; };
+
+// Two NLoaders for the two 128-column halves of a 256-column A tile.
+template <class C>
+struct NLoaderWide {
+  using T = typename C::elem;
+  NLoader<C, 0> h0;
+  NLoader<C, C::NT / 2> h1;
+  static constexpr int NI = 2 * NLoader<C, 0>::NI;
+  static constexpr int WRITES = NI;
+  __device__ __forceinline__ void init(int mn_valid, int kvalid) {
+    h0.init(mn_valid, kvalid);
+    h1.init(mn_valid - 128, kvalid);
+  }
+  template <int SET>
+  __device__ __forceinline__ void store(T* lds) {
+    h0.template store<SET>(lds);
+    h1.template store<SET>(lds + 128 * C::BK);
+  }
+};
+
 template <class C, bool GATE_UP, typename OutT>
 __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_long_kernel(GArgs g) {
   GEMM_PROLOGUE(C)
-  static_assert(C::BM == 128 && C::BN == 128, "[k][128] operand tiles");
+  static_assert(C::BM == 256 && C::BN == 128 && WideA<C>::value, "A: two [k][128] halves; B: [k][128]");
   const int I = g.I, H = g.H;
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
   const int lda = M, ldb = N;   // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
@@ -1676,25 +1709,23 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_long_kernel(GArgs g) {
     const int gm = min(kRowTileGroup, ntm - grp * kRowTileGroup);
     const int nt = rem / gm, mt = grp * kRowTileGroup + (rem - nt * gm);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
-    NLoader<C, 0> al;
-    NLoader<C, C::NT / 2> bl;
+    NLoaderWide<C> al;
+    NLoader<C, C::NT / 4> bl;
     al.init(M - m0, cnt);
     bl.init(N - n0, cnt);
     const T* Ap = Ag + (size_t)off * lda + m0;
+    const T* Ap1 = Ap + (M - m0 > 128 ? 128 : 0);   // second half (in range even when it is all masked)
     const T* Bp = Bg + (size_t)off * ldb + n0;
     auto aload = [&](auto& ld, int kt, auto set) {
-      ld.template load<decltype(set)::value>(kt, [&](int k) { return Ap + (size_t)k * lda; });
+      constexpr int SET = decltype(set)::value;
+      ld.h0.template load<SET>(kt, [&](int k) { return Ap + (size_t)k * lda; });
+      ld.h1.template load<SET>(kt, [&](int k) { return Ap1 + (size_t)k * lda; });
     };
     auto bload = [&](auto& ld, int kt, auto set) {
       ld.template load<decltype(set)::value>(kt, [&](int k) { return Bp + (size_t)k * ldb; });
     };
     f32x16 acc[C::FM][C::FN];
-    // gate_up (45 x 23 tiles per expert at the gpt-oss shapes) runs faster
-    // with the one-set loop (Zipf batch 5.16 -> 4.84 ms; no spills, 170
-    // VGPRs), down (23 x 23) with two sets (2.49 against 2.61 ms; 7 VGPRs
-    // spilled)
-    if constexpr (GATE_UP) mainloop_pf1<C, true, true>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
-    else mainloop<C, true, true>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
+    mainloop<C, true, true>(al, bl, aload, bload, (cnt + C::BK - 1) / C::BK, lds, acc);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
@@ -1939,7 +1970,7 @@ constexpr int kLongMin = 1024;
 
 template <bool GU, typename OutT>
 static hipError_t wgrad_long_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
-  using C = CfgB;
+  using C = CfgL;
   const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
   GArgs g = base_args(pb, C::BM);
   g.A = A; g.B = B; g.out0 = dW;
