@@ -654,13 +654,14 @@ __device__ __forceinline__ bool row_tile(const GArgs& g, int& e, int& m0, int& r
   return true;
 }
 
-// Weight-gradient tiles: chunks of 8 consecutive tiles are dealt round-robin
-// to the XCDs (experts longest first), so every XCD gets a similar share of
-// long and short experts and a chunk's tiles share operands in one L2.  The
-// j-th tile of this workgroup's XCD, or -1 past the end.
+// Weight-gradient tiles: chunks of CH consecutive tiles are dealt
+// round-robin to the XCDs (experts longest first), so every XCD gets a
+// similar share of long and short experts and a chunk's tiles share operands
+// in one L2.  The j-th tile of this workgroup's XCD, or -1 past the end.
+template <int CH>
 __device__ __forceinline__ int dealt_tile(int j, int total) {
   const int x = blockIdx.x & 7;
-  const int t = (((j >> 3) << 3) + x) * 8 + (j & 7);
+  const int t = ((j / CH) * 8 + x) * CH + j % CH;
   return t < total ? t : -1;
 }
 
@@ -1645,12 +1646,12 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
 // the token-row engine's two-set pipeline (8 waves of 64 x 64, one workgroup
 // per CU), both operands position-major and read with transposing LDS reads
 // (B as one [k][128] tile, A as two; 128 x 128 tiles at two workgroups per
-// CU were 6 % slower).  A persistent grid deals chunks of 8 tiles round-robin to the XCDs,
-// so each XCD gets a share of every expert (one hot expert can hold a fifth
-// of all positions; contiguous ranges per XCD left one XCD with a third of
-// the work, 2x slower).  Inside an expert, groups of 8 M-tiles run N-tile by
-// N-tile, so a chunk's 8 tiles share their B row block and an XCD's chunks
-// of one group share the A row blocks in its L2.  The tiled kernel, built
+// CU were 6 % slower).  A persistent grid deals chunks of 32 tiles
+// round-robin to the XCDs, so each XCD gets a share of every expert (one hot
+// expert can hold a fifth of all positions; contiguous ranges per XCD left
+// one XCD with a third of the work, 2x slower).  Inside an expert, groups of
+// 8 M-tiles run N-tile by N-tile, so a chunk's tiles share 4 B row blocks
+// and 8 A row blocks in one L2.  The tiled kernel, built
 // around short K loops and the dW store stream, took these experts at ~550
 // TFLOP/s.
 // 256 x 128 tiles on 8 waves (64 x 64 each), one workgroup per CU; the A
@@ -1696,10 +1697,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_long_kernel(GArgs g) {
   const T* Ag = (const T*)g.A;
   const T* Bg = (const T*)g.B;
   OutT* dW = (OutT*)g.out0;
-  // this XCD's j-th tile: chunks of 8 consecutive tiles dealt round-robin to
-  // the XCDs (increasing in j, so the first one past the end ends the loop)
+  // this XCD's j-th tile: chunks of 32 consecutive tiles (an XCD's 32
+  // workgroups; 4 N-tiles of one group of 8 M-tiles) dealt round-robin to
+  // the XCDs, increasing in j, so the first one past the end ends the loop.
+  // Chunks of 8 tiles: gate_up 4.52 against 4.30-4.35 ms on the Zipf batch.
   for (int j = blockIdx.x >> 3;; j += K) {
-    const int t = dealt_tile(j, total);
+    const int t = dealt_tile<32>(j, total);
     if (t < 0) break;
     const int er = t / per_e, local = t - er * per_e;
     const int e = g.expert_order[er];
