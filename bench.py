@@ -98,7 +98,7 @@ def measured_traffic(kernel, workload, grad_dtype):
 
 # ------------------------------------------------------------------ per-kernel model
 RES_KMAX = 240   # the resident-operand weight gradient's limit (positions per expert)
-LONG_MIN = 1024  # experts with more positions take the long-K weight gradient
+LONG_MIN = 512  # experts with more positions take the long-K weight gradient
 def kernel_model(wl, counts, grad_bytes):
     """Algorithmic bytes and flops of one launch of each kernel.
 

@@ -1968,8 +1968,11 @@ static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const voi
   });
 }
 
-// Experts with more than kLongMin positions take the long-K kernel.
-constexpr int kLongMin = 1024;
+// Experts with more than kLongMin positions take the long-K kernel (Zipf
+// batch weight gradients: 8.87 ms at 512, 8.95 at 384, 9.16 at 1024; at 256
+// the backward workload's 257-296-position experts were slower than on the
+// tiled kernel, 7.34 against 6.15 ms).
+constexpr int kLongMin = 512;
 
 template <bool GU, typename OutT>
 static hipError_t wgrad_long_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {

@@ -133,10 +133,10 @@ def check_sampled_expert(r, which):
     nonempty = [e for e in np.argsort(counts, kind="stable") if counts[e] > 0]
     # resident_max / tiled_min: the experts on either side of the resident
     # weight-gradient kernel's limit of 240 positions; long_min: the smallest
-    # expert above the long-K kernel's threshold of 1024 positions
+    # expert above the long-K kernel's threshold of 512 positions
     below = [x for x in nonempty if counts[x] <= 240]
     above = [x for x in nonempty if counts[x] > 240]
-    long_ = [x for x in nonempty if counts[x] > 1024]
+    long_ = [x for x in nonempty if counts[x] > 512]
     pick = {"coldest": lambda: nonempty[0], "median": lambda: nonempty[len(nonempty) // 2],
             "hottest": lambda: nonempty[-1], "resident_max": lambda: below[-1], "tiled_min": lambda: above[0],
             "long_min": lambda: long_[0]}

@@ -207,12 +207,12 @@ def test_large_experts_ragged(act, layout):
 
 @pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
 def test_weight_grad_expert_sizes(grad_dtype):
-    """Experts of 0, 1, 16, 17, 208, 209, 240, 241, 256, 257, 1024, 1025 and
+    """Experts of 0, 1, 16, 17, 208, 209, 240, 241, 256, 257, 512, 513 and
     1601 slots: the resident-operand weight gradient takes experts of up to
     240 slots (k-slices of 16, zeros for an empty expert), the long-K one
-    those above 1024 (ragged last k-step) and the tiled one the rest, all in
+    those above 512 (ragged last k-step) and the tiled one the rest, all in
     one call, for bf16 and for fp32 gradient storage."""
-    counts = [1601, 1025, 1024, 256, 257, 240, 241, 208, 209, 1, 16, 17, 0]
+    counts = [1601, 513, 512, 256, 257, 240, 241, 208, 209, 1, 16, 17, 0]
     E, K = len(counts), 1
     T, H, I = sum(counts), 264, 200
     rng = np.random.default_rng(31)

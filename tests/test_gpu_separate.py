@@ -37,10 +37,10 @@ def test_separate_weights_match_oracle(act, layout, dtype, grad_dtype, save):
 @pytest.mark.parametrize("layout", ["concat", "interleaved"])
 @pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
 def test_separate_weights_all_weight_gradient_kernels(layout, grad_dtype):
-    """Experts of 0, 16, 240, 241, 300, 1025 and 1601 slots: the resident,
+    """Experts of 0, 16, 240, 241, 300, 513 and 1601 slots: the resident,
     tiled and long-K weight gradients each write rows of the separate gate
     and up tensors (tiles straddling their boundary at I = 200)."""
-    counts = [1601, 1025, 300, 241, 240, 16, 0]
+    counts = [1601, 513, 300, 241, 240, 16, 0]
     E, K = len(counts), 1
     T, H, I = sum(counts), 264, 200
     rng = np.random.default_rng(41)
