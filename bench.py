@@ -6,9 +6,15 @@ permutation, gate_up projection with the gated activation, down projection
 with the routing weight, per-token combine, then the backward's input
 gradients, routing-weight gradients and weight gradients.
 
+The default workload is the largest one that fits one GPU: the gpt-oss layer
+shape (H = I = 2880, E = 128, top-4, clamped GLU) at T = 32768 tokens with
+Zipf(1.2) expert popularity, forward plus backward.
+
 Prints one JSON line.  `value` is useful routed TFLOP/s over the whole step:
 forward 6*S*H*I plus backward 12*S*H*I floating-point operations (S = T*K),
-with inputs and weights resident in HBM before the timed region starts.
+with inputs and weights resident in HBM before the timed region starts.  The
+timed region records no per-kernel events; a second, instrumented pass over
+the same steps gives each kernel's average launch time for `roofline`.
 """
 from __future__ import annotations
 
@@ -31,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="gptoss", help="synthetic workload name (synth.WORKLOADS)")
+    p.add_argument("--workload", default="zipf", help="synthetic workload name (synth.WORKLOADS)")
     p.add_argument("--grad-dtype", default="bf16", choices=["fp32", "bf16"],
                    help="weight-gradient storage (accumulation is fp32 either way); bf16 is the parameter dtype")
     p.add_argument("--no-alt-grad-dtype", action="store_true",
@@ -100,10 +106,17 @@ def measured_traffic(kernel, workload, grad_dtype):
 RES_KMAX = 240   # the resident-operand weight gradient's limit (positions per expert)
 LONG_MIN = 512  # experts with more positions take the long-K weight gradient
 def kernel_model(wl, counts, grad_bytes):
-    """Algorithmic bytes and flops of one launch of each kernel.
+    """Algorithmic bytes and routed flops of one launch of each kernel.
 
-    Bytes count each distinct input element read once and each output element
-    written once; only experts that receive slots have their weights read.
+    Bytes are the layer's own inputs and outputs that the kernel must move,
+    each element once: the weights of the experts that receive slots (read by
+    the projections and their input gradients), the hidden states and output
+    gradient rows (read), and the weight gradients (written).  The per-slot
+    intermediates (the activation, Z, dZ, the permuted rows, the per-slot
+    expert outputs) are implementation traffic and are not counted, except
+    for the data-movement kernels (combine, row gather, routing-weight
+    reduce), whose whole work is moving them.  Flops count the routed work
+    only (2*M*N*K per product over the slots).
     """
     S, T, H, I = wl.S, wl.T, wl.H, wl.I
     eb = 2 if wl.dtype == "bf16" else 4
@@ -111,11 +124,12 @@ def kernel_model(wl, counts, grad_bytes):
     Wgu = touched * 2 * I * H * eb
     Wd = touched * H * I * eb
     m = {
-        "gate_up_glu": (Wgu + T * H * eb + S * I * eb + S * 2 * I * 4, 4.0 * S * H * I),
-        "down_weighted": (Wd + S * I * eb + S * H * 4 + S * 4, 2.0 * S * H * I),
+        "gate_up_glu": (Wgu + T * H * eb, 4.0 * S * H * I),
+        "down_weighted": (Wd, 2.0 * S * H * I),
         "combine": (S * H * 4 + T * H * eb + S * 4, 0.0),
-        "down_dgrad_glu_bwd": (Wd + T * H * eb + S * 2 * I * 4 + S * 2 * I * eb + S * I * eb, 2.0 * S * H * I),
-        "gate_up_dgrad": (Wgu + S * 2 * I * eb + S * H * 4, 4.0 * S * H * I),
+        "gather_rows": (2 * S * H * eb + S * 4, 0.0),
+        "down_dgrad_glu_bwd": (Wd + T * H * eb, 2.0 * S * H * I),
+        "gate_up_dgrad": (Wgu, 4.0 * S * H * I),
         "topkw_reduce": (S * 4 * 2, 0.0),
     }
     # Weight gradients.  With bf16 operands, experts with at most RES_KMAX
@@ -123,13 +137,14 @@ def kernel_model(wl, counts, grad_bytes):
     # named wgrad_down / wgrad_gate_up, those with more than LONG_MIN the
     # long-K kernel (*_long) and the rest the tiled kernel (*_hot); with fp32
     # operands the tiled kernel takes every expert under the plain names.
-    # Token-row reads are prorated by the positions each covers.
+    # Each writes its experts' gradients; the hidden / output-gradient rows it
+    # reads are prorated by the positions it covers.
     def wgrad(sel):
         s_part = int(counts[sel].sum())
         e_part = int(sel.sum())
         tok = s_part / S if S else 0.0
-        down = (tok * T * H * eb + s_part * I * eb + e_part * H * I * grad_bytes, 2.0 * s_part * H * I)
-        gu = (s_part * 2 * I * eb + tok * T * H * eb + e_part * 2 * I * H * grad_bytes, 4.0 * s_part * H * I)
+        down = (tok * T * H * eb + e_part * H * I * grad_bytes, 2.0 * s_part * H * I)
+        gu = (tok * T * H * eb + e_part * 2 * I * H * grad_bytes, 4.0 * s_part * H * I)
         return down, gu
     if wl.dtype == "bf16":
         small = counts <= RES_KMAX
@@ -146,6 +161,9 @@ def kernel_model(wl, counts, grad_bytes):
 
 
 def roofline_for(name, avg_ms, model):
+    """Achieved rate of one kernel against the roof that bounds it: MFMA when
+    its routed flops take longer at the bf16 dense peak than its algorithmic
+    bytes at the HBM peak, else HBM."""
     nbytes, flops = model[name]
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
@@ -552,10 +570,7 @@ def main():
         fwd_ms.append(ev[0].elapsed_time(ev[1]))
         bwd_ms.append(ev[1].elapsed_time(ev[2]))
 
-    # timed region: exactly `steps` steps, with per-kernel HIP events on the launch stream
-    timing = not args.no_kernel_timing
-    if timing:
-        moe.timing_enable(64 * args.steps)
+    # timed region: exactly `steps` steps, nothing recorded between the launches
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -564,11 +579,19 @@ def main():
     t_stop.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    print(f"[bench] {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # instrumented pass over the same number of steps: HIP events recorded on
+    # the launch stream around every kernel give each kernel's average launch
+    # time (for `roofline` and `kernels_avg_ms`)
     kernels = {}
-    if timing:
+    if not args.no_kernel_timing:
+        moe.timing_enable(64 * args.steps)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
         kernels = {k: (n, ms) for k, (n, ms) in moe.timing_read().items()}
         moe.timing_disable()
-    print(f"[bench] {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     S, H, I = wl.S, wl.H, wl.I
     flops_fwd, flops_bwd = 6.0 * S * H * I, 12.0 * S * H * I
@@ -629,8 +652,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: routed MoE layer forward+backward, T={wl.T} H={wl.H} I={wl.I} "
                                f"E={wl.E} top-{wl.K}, {wl.act} GLU, gate/up {wl.layout}, "
-                               f"{wl.routing} routing, {args.grad_dtype} weight grads "
-                               f"(fp32 accumulation), saved Z",
+                               f"{wl.routing} routing"
+                               + (f" (s={wl.zipf_s})" if wl.routing == "zipf" else "")
+                               + f", {args.grad_dtype} weight grads (fp32 accumulation), saved Z",
                    "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K, "parallelism": "single GPU"},
         "fwd_ms": round(fm, 4),
         "bwd_ms": round(bm, 4),

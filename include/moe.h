@@ -46,10 +46,13 @@
  *     MOE_ERR_UNSUPPORTED (H or I not a multiple of 8, E > 1024, K > 64,
  *     S >= 2^31), MOE_ERR_WORKSPACE (ws_bytes below the required size).
  *     A failed kernel launch returns MOE_ERR_HIP.
- *   - An expert id outside [0,E) is found on the device: its slot is dropped
- *     from every sum, a flag is set in the workspace, and
- *     moe_check_device_status reports MOE_ERR_BAD_EXPERT_ID; the outputs of
- *     that call are then unspecified.
+ *   - An expert id outside [0,E) is found on the device and its slot is
+ *     dropped: out, d_hidden and the weight gradients are those of the same
+ *     call with that slot's routing weight set to zero, its d_topk_weights
+ *     entry is 0, and routing places it after every valid slot (inv_pos -1).
+ *     A count is kept in the workspace and moe_check_device_status reports
+ *     MOE_ERR_BAD_EXPERT_ID.  No memory outside the caller's buffers is
+ *     touched for such an id.
  *   - T = 0 is valid: nothing is launched for the activations; the forward
  *     and backward entry points and moe_router clear the workspace status
  *     word (so moe_check_device_status reports MOE_OK for the call), and the
@@ -97,7 +100,8 @@ typedef struct {
 
 /* Sizes in bytes of the workspaces moe_fwd and moe_bwd need, and of the
  * optional `saved` buffer (the gate_up projection outputs Z, fp32 [S,2I] in
- * expert-sorted slot order) that moe_fwd can fill for moe_bwd.  Any output pointer may be NULL.
+ * expert-sorted slot order) that moe_fwd can fill for moe_bwd.  Any output
+ * pointer may be NULL.
  * The routing part of both workspaces is moe_route_workspace_size(). */
 moe_status_t moe_workspace_size(const moe_desc_t* desc, size_t* fwd_ws,
                                 size_t* bwd_ws, size_t* saved_bytes);
@@ -108,7 +112,8 @@ moe_status_t moe_route_workspace_size(const moe_desc_t* desc, size_t* route_ws);
  * Outputs (device, int32):
  *   counts[E]       slots routed to each expert
  *   offsets[E+1]    exclusive prefix sum of counts
- *   sorted_slot[S]  slots in expert order; ascending slot id inside an expert
+ *   sorted_slot[S]  slots in expert order; ascending slot id inside an expert;
+ *                   slots with an id outside [0,E) last, in ascending order
  *   inv_pos[S]      position of slot s in sorted_slot (-1 for a bad id)
  * Bit-exact and deterministic.  Any of the four outputs may be NULL (then not
  * written).  ws: at least moe_route_workspace_size() bytes. */
@@ -145,13 +150,15 @@ moe_status_t moe_router(const moe_desc_t* desc, const float* logits,
 /* Forward: out [T,H] = sum_k w[t,k] * FFN_{ids[t,k]}(hidden[t]).
  * Routing, gate_up projection with the gated activation, down projection with
  * the routing weight, and a deterministic per-token sum over the K slots
- * (fp32, k order, one rounding).  `saved` may be NULL; if given (saved_bytes
- * from moe_workspace_size) it receives Z for moe_bwd. */
+ * (fp32, k order, one rounding).  `saved` may be NULL; if given, it receives
+ * Z for moe_bwd and `saved_bytes` (its size) must be at least the
+ * saved_bytes of moe_workspace_size, else MOE_ERR_WORKSPACE (nothing
+ * launched). */
 moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden,
                      const int32_t* topk_ids, const float* topk_weights,
                      const void* w_gate_up, const void* w_down, void* out,
-                     void* saved, void* ws, size_t ws_bytes,
-                     hipStream_t stream);
+                     void* saved, size_t saved_bytes, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* Backward of moe_fwd given d_out = dL/dout [T,H]:
  *   d_hidden [T,H], d_topk_weights fp32 [T,K] (<d_out[t], expert output of
@@ -159,23 +166,27 @@ moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden,
  *   w_gate_up's layout), d_w_down [E,H,I].  Weight gradients are accumulated
  *   in fp32 over the tokens and stored in grad_dtype; an expert with no slots
  *   gets exact zeros.  `saved` is the buffer moe_fwd filled for the same
- *   inputs, or NULL (then Z is recomputed). */
+ *   inputs, or NULL (then Z is recomputed); when given, `saved_bytes` (its
+ *   size) must be at least moe_workspace_size's saved_bytes, else
+ *   MOE_ERR_WORKSPACE (nothing launched). */
 moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden,
                      const int32_t* topk_ids, const float* topk_weights,
                      const void* w_gate_up, const void* w_down,
-                     const void* d_out, const void* saved, void* d_hidden,
-                     float* d_topk_weights, void* d_w_gate_up, void* d_w_down,
-                     void* ws, size_t ws_bytes, hipStream_t stream);
+                     const void* d_out, const void* saved, size_t saved_bytes,
+                     void* d_hidden, float* d_topk_weights, void* d_w_gate_up,
+                     void* d_w_down, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* Forward from router logits [T,E] (fp32): moe_router's top-k and weights
  * (written to topk_ids [T,K] and topk_weights [T,K] for the backward), then
- * moe_fwd on them in the same call.  Same outputs, workspace, `saved` and
- * errors as moe_fwd (plus K <= E). */
+ * moe_fwd on them in the same call.  Same outputs, workspace, `saved` /
+ * `saved_bytes` and errors as moe_fwd (plus K <= E). */
 moe_status_t moe_fwd_logits(const moe_desc_t* desc, const void* hidden,
                             const float* logits, const void* w_gate_up,
                             const void* w_down, void* out, int32_t* topk_ids,
-                            float* topk_weights, void* saved, void* ws,
-                            size_t ws_bytes, hipStream_t stream);
+                            float* topk_weights, void* saved,
+                            size_t saved_bytes, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* Gradient of the router's weights with respect to its logits, given
  * d_topk_weights fp32 [T,K] (from moe_bwd): d_logits fp32 [T,E] with
@@ -200,16 +211,17 @@ moe_status_t moe_router_bwd(const moe_desc_t* desc, const int32_t* topk_ids,
 moe_status_t moe_fwd_sep(const moe_desc_t* desc, const void* hidden,
                          const int32_t* topk_ids, const float* topk_weights,
                          const void* w_gate, const void* w_up,
-                         const void* w_down, void* out, void* saved, void* ws,
-                         size_t ws_bytes, hipStream_t stream);
+                         const void* w_down, void* out, void* saved,
+                         size_t saved_bytes, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 moe_status_t moe_bwd_sep(const moe_desc_t* desc, const void* hidden,
                          const int32_t* topk_ids, const float* topk_weights,
                          const void* w_gate, const void* w_up,
                          const void* w_down, const void* d_out,
-                         const void* saved, void* d_hidden,
-                         float* d_topk_weights, void* d_w_gate, void* d_w_up,
-                         void* d_w_down, void* ws, size_t ws_bytes,
-                         hipStream_t stream);
+                         const void* saved, size_t saved_bytes,
+                         void* d_hidden, float* d_topk_weights, void* d_w_gate,
+                         void* d_w_up, void* d_w_down, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
 
 /* Synchronises `stream` and reports MOE_ERR_BAD_EXPERT_ID if the last
  * routing done in `ws` met an id outside [0,E), else MOE_OK. */

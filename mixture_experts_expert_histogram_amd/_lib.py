@@ -60,12 +60,12 @@ def library() -> ctypes.CDLL:
     lib.moe_route_workspace_size.argtypes = [pd, psz]
     lib.moe_route.argtypes = [pd, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_router.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.moe_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.moe_fwd_logits.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.moe_fwd_logits.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.moe_router_bwd.argtypes = [pd, vp, vp, vp, vp, vp]
-    lib.moe_fwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.moe_bwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.moe_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_fwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.moe_bwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_check_device_status.argtypes = [vp, vp]
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -121,6 +121,10 @@ def route_workspace_size(desc: MoeDesc) -> int:
 # ---------------------------------------------------------------- torch layer
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream():
@@ -238,8 +242,9 @@ def fwd_logits(hidden, logits, K: int, w_gate_up, w_down, act="swiglu", layout="
     if save and saved is None:
         saved = empty_workspace(sbytes, dev)
     _check(library().moe_fwd_logits(ctypes.byref(d), _ptr(hidden), _ptr(lg), _ptr(w_gate_up), _ptr(w_down),
-                                    _ptr(out), _ptr(ids), _ptr(w), _ptr(saved) if save else None, _ptr(ws),
-                                    ws.numel(), _stream()), "moe_fwd_logits")
+                                    _ptr(out), _ptr(ids), _ptr(w), _ptr(saved) if save else None,
+                                    _nbytes(saved) if save else 0, _ptr(ws), ws.numel(), _stream()),
+           "moe_fwd_logits")
     return out, ids, w, (saved if save else None), ws
 
 
@@ -255,7 +260,8 @@ def fwd(hidden, topk_ids, topk_weights, w_gate_up, w_down, act="swiglu", layout=
     if save and saved is None:
         saved = empty_workspace(sbytes, hidden.device)
     _check(library().moe_fwd(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate_up), _ptr(w_down),
-                             _ptr(out), _ptr(saved) if save else None, _ptr(ws), ws.numel(), _stream()), "moe_fwd")
+                             _ptr(out), _ptr(saved) if save else None, _nbytes(saved) if save else 0, _ptr(ws),
+                             ws.numel(), _stream()), "moe_fwd")
     return out, (saved if save else None), ws
 
 
@@ -277,8 +283,8 @@ def bwd(hidden, topk_ids, topk_weights, w_gate_up, w_down, d_out, saved=None, ac
                  torch.empty(w_down.shape, dtype=gdt, device=hidden.device))
     dh, dw, dgu, dd = grads
     _check(library().moe_bwd(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate_up), _ptr(w_down),
-                             _ptr(d_out.contiguous()), _ptr(saved), _ptr(dh), _ptr(dw), _ptr(dgu), _ptr(dd),
-                             _ptr(ws), ws.numel(), _stream()), "moe_bwd")
+                             _ptr(d_out.contiguous()), _ptr(saved), _nbytes(saved), _ptr(dh), _ptr(dw), _ptr(dgu),
+                             _ptr(dd), _ptr(ws), ws.numel(), _stream()), "moe_bwd")
     return dh, dw, dgu, dd, ws
 
 
@@ -310,8 +316,8 @@ def fwd_sep(hidden, topk_ids, topk_weights, w_gate, w_up, w_down, act="swiglu", 
     if save and saved is None:
         saved = empty_workspace(sbytes, hidden.device)
     _check(library().moe_fwd_sep(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate), _ptr(w_up),
-                                 _ptr(w_down), _ptr(out), _ptr(saved) if save else None, _ptr(ws), ws.numel(),
-                                 _stream()), "moe_fwd_sep")
+                                 _ptr(w_down), _ptr(out), _ptr(saved) if save else None,
+                                 _nbytes(saved) if save else 0, _ptr(ws), ws.numel(), _stream()), "moe_fwd_sep")
     return out, (saved if save else None), ws
 
 
@@ -332,8 +338,9 @@ def bwd_sep(hidden, topk_ids, topk_weights, w_gate, w_up, w_down, d_out, saved=N
                  torch.empty(w_down.shape, dtype=gdt, device=hidden.device))
     dh, dw, dg, du, dd = grads
     _check(library().moe_bwd_sep(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate), _ptr(w_up),
-                                 _ptr(w_down), _ptr(d_out.contiguous()), _ptr(saved), _ptr(dh), _ptr(dw), _ptr(dg),
-                                 _ptr(du), _ptr(dd), _ptr(ws), ws.numel(), _stream()), "moe_bwd_sep")
+                                 _ptr(w_down), _ptr(d_out.contiguous()), _ptr(saved), _nbytes(saved), _ptr(dh),
+                                 _ptr(dw), _ptr(dg), _ptr(du), _ptr(dd), _ptr(ws), ws.numel(), _stream()),
+           "moe_bwd_sep")
     return dh, dw, dg, du, dd, ws
 
 

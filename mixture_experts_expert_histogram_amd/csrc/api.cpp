@@ -87,6 +87,9 @@ RouteState route_state(void* ws, const Layout& L, const Dims& d) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Bytes of the optional `saved` buffer: Z fp32 [S,2I] in expert-sorted order.
+size_t saved_size(const Dims& d) { return (size_t)d.S * 2 * d.I * sizeof(float); }
+
 // Shape and enum checks shared by every entry point.
 moe_status_t check_desc(const moe_desc_t* desc, Dims* d) {
   if (!desc) return MOE_ERR_INVALID_ARG;
@@ -195,7 +198,7 @@ moe_status_t moe_workspace_size(const moe_desc_t* desc, size_t* fwd_ws, size_t* 
   const Layout L = make_layout(d);
   if (fwd_ws) *fwd_ws = L.f_end;
   if (bwd_ws) *bwd_ws = L.b_end;
-  if (saved_bytes) *saved_bytes = (size_t)d.S * 2 * d.I * sizeof(float);
+  if (saved_bytes) *saved_bytes = saved_size(d);
   return MOE_OK;
 }
 
@@ -268,32 +271,34 @@ moe_status_t moe_router_bwd(const moe_desc_t* desc, const int32_t* topk_ids, con
 static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                              const float* topk_weights, const float* logits, int32_t* ids_out, float* w_out,
                              const void* w_gate_up, const void* w_up, const void* w_down, void* out, void* saved,
-                             void* ws, size_t ws_bytes, hipStream_t stream);
+                             size_t saved_bytes, void* ws, size_t ws_bytes, hipStream_t stream);
 
 moe_status_t moe_fwd(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                      const float* topk_weights, const void* w_gate_up, const void* w_down, void* out, void* saved,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
+                     size_t saved_bytes, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (desc && desc->T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
   return fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate_up, nullptr, w_down, out,
-                  saved, ws, ws_bytes, stream);
+                  saved, saved_bytes, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_fwd_sep(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                          const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
-                         void* out, void* saved, void* ws, size_t ws_bytes, hipStream_t stream) {
+                         void* out, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   if (desc && desc->T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
   if (!w_up) return MOE_ERR_INVALID_ARG;
   return fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate, w_up, w_down, out, saved,
-                  ws, ws_bytes, stream);
+                  saved_bytes, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_fwd_logits(const moe_desc_t* desc, const void* hidden, const float* logits,
                             const void* w_gate_up, const void* w_down, void* out, int32_t* topk_ids,
-                            float* topk_weights, void* saved, void* ws, size_t ws_bytes, hipStream_t stream) {
+                            float* topk_weights, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
   if (desc && desc->T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
   if (desc && desc->K > desc->E) return MOE_ERR_INVALID_ARG;
   return fwd_impl(desc, hidden, topk_ids, topk_weights, logits, topk_ids, topk_weights, w_gate_up, nullptr, w_down,
-                  out, saved, ws, ws_bytes, stream);
+                  out, saved, saved_bytes, ws, ws_bytes, stream);
 }
 
 // Forward from given ids and weights (logits == NULL) or from router logits
@@ -302,7 +307,7 @@ moe_status_t moe_fwd_logits(const moe_desc_t* desc, const void* hidden, const fl
 static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                              const float* topk_weights, const float* logits, int32_t* ids_out, float* w_out,
                              const void* w_gate_up, const void* w_up, const void* w_down, void* out, void* saved,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+                             size_t saved_bytes, void* ws, size_t ws_bytes, hipStream_t stream) {
   Dims d;
   moe_status_t st = check_desc(desc, &d);
   if (st != MOE_OK) return st;
@@ -313,6 +318,7 @@ static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const i
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
   if (ws_bytes < L.f_end) return MOE_ERR_WORKSPACE;
+  if (saved && saved_bytes < saved_size(d)) return MOE_ERR_WORKSPACE;
   if (d.T == 0) {   // nothing to route: clear the status word so it reports this call
     HIP_TRY(launch_fill_zero((char*)ws + L.status, 4 * sizeof(int32_t), stream));
     return MOE_OK;
@@ -340,9 +346,9 @@ static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const i
 // [E,I,H] and w_up / d_w_up the up tensors.
 static moe_status_t bwd_impl(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                              const float* topk_weights, const void* w_gate_up, const void* w_up, const void* w_down,
-                             const void* d_out, const void* saved, void* d_hidden, float* d_topk_weights,
-                             void* d_w_gate_up, void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             const void* d_out, const void* saved, size_t saved_bytes, void* d_hidden,
+                             float* d_topk_weights, void* d_w_gate_up, void* d_w_up, void* d_w_down, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   Dims d;
   moe_status_t st = check_desc(desc, &d);
   if (st != MOE_OK) return st;
@@ -355,6 +361,7 @@ static moe_status_t bwd_impl(const moe_desc_t* desc, const void* hidden, const i
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(d);
   if (ws_bytes < L.b_end) return MOE_ERR_WORKSPACE;
+  if (saved && saved_bytes < saved_size(d)) return MOE_ERR_WORKSPACE;
   if (d.T == 0) {   // no slots: zero weight gradients, and a status word that reports this call
     HIP_TRY(launch_fill_zero((char*)ws + L.status, 4 * sizeof(int32_t), stream));
     if (w_up) {
@@ -401,19 +408,19 @@ static moe_status_t bwd_impl(const moe_desc_t* desc, const void* hidden, const i
 
 moe_status_t moe_bwd(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                      const float* topk_weights, const void* w_gate_up, const void* w_down, const void* d_out,
-                     const void* saved, void* d_hidden, float* d_topk_weights, void* d_w_gate_up, void* d_w_down,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
-  return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate_up, nullptr, w_down, d_out, saved, d_hidden,
-                  d_topk_weights, d_w_gate_up, nullptr, d_w_down, ws, ws_bytes, stream);
+                     const void* saved, size_t saved_bytes, void* d_hidden, float* d_topk_weights,
+                     void* d_w_gate_up, void* d_w_down, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate_up, nullptr, w_down, d_out, saved, saved_bytes,
+                  d_hidden, d_topk_weights, d_w_gate_up, nullptr, d_w_down, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_bwd_sep(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
                          const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
-                         const void* d_out, const void* saved, void* d_hidden, float* d_topk_weights,
-                         void* d_w_gate, void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         const void* d_out, const void* saved, size_t saved_bytes, void* d_hidden,
+                         float* d_topk_weights, void* d_w_gate, void* d_w_up, void* d_w_down, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   if (!w_up || !d_w_up) return MOE_ERR_INVALID_ARG;
-  return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate, w_up, w_down, d_out, saved, d_hidden,
+  return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate, w_up, w_down, d_out, saved, saved_bytes, d_hidden,
                   d_topk_weights, d_w_gate, d_w_up, d_w_down, ws, ws_bytes, stream);
 }
 

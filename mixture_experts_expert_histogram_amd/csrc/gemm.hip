@@ -21,6 +21,7 @@
 #include "moe_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace moe {
@@ -1096,6 +1097,13 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
   const int lda = M, ldb = N;       // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
   OutT* dW = (OutT*)g.out0;
+  // The host cannot tell without a sync whether any expert falls in this
+  // kernel's range of positions; when the hottest expert does not, leave
+  // before touching the tables.
+  if (g.small_max >= 0) {
+    const int e0 = g.expert_order[0];
+    if (g.offsets[e0 + 1] - g.offsets[e0] <= g.small_max) return;
+  }
   __shared__ WgradTables tab;
   for (int i = threadIdx.x; i <= g.E; i += C::NT + kStoreThreads) {
     if (i < g.E) tab.order[i] = g.expert_order[i];
@@ -1686,6 +1694,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void wgrad_long_kernel(GArgs g) {
   const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
   const int lda = M, ldb = N;   // GATE_UP: dZ [S,2I], Xp [S,H]; else dYp [S,H], aw [S,I]
   int l = 0, h = g.E;           // nhot = leading experts with more than hot_min positions
+  {                             // none (the host cannot tell without a sync): leave at once
+    const int e0 = g.expert_order[0];
+    if (g.offsets[e0 + 1] - g.offsets[e0] <= g.hot_min) return;
+  }
   while (l < h) {
     const int mid = (l + h) >> 1;
     const int e = g.expert_order[mid];
@@ -1916,11 +1928,21 @@ hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const voi
                        : gate_up_dgrad_impl<CfgB>(pb, dZ, Wgu, dXp, s);
 }
 
+// Compute units of the current device, looked up once per device (the
+// persistent weight-gradient grids hold one workgroup per CU).
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_device_cus[kMaxDevices];
 static int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    return 8;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 8;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int c = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 8;
+  if (cached) g_device_cus[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -1946,7 +1968,7 @@ static hipError_t wgrad_impl(const GemmProblem& pb, const void* A, const void* B
   g.small_max = small_max;
   g.hot_min = hot_min;
   // one persistent workgroup per CU, a whole number per XCD
-  static const int cus = device_cus();
+  const int cus = device_cus();
   const long grid = (cus / 8) * 8;
   const char* name = small_max >= 0 ? (GU ? "wgrad_gate_up_hot" : "wgrad_down_hot")
                                     : (GU ? "wgrad_gate_up" : "wgrad_down");
@@ -1961,7 +1983,7 @@ static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const voi
   GArgs g = base_args(pb, 128);
   g.A = A; g.B = B; g.out0 = dW;
   if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
-  static const int cus = device_cus();
+  const int cus = device_cus();
   const long grid = (cus / 8) * 8;
   return run_kernel(GU ? "wgrad_gate_up" : "wgrad_down", s, [&] {
     wgrad_res_kernel<GU, OutT, kResKmax><<<grid, kResThreads, 0, s>>>(g);
@@ -1985,7 +2007,7 @@ static hipError_t wgrad_long_impl(const GemmProblem& pb, const void* A, const vo
   g.ntn = (N + C::BN - 1) / C::BN;
   g.hot_min = kLongMin;
   // persistent: C::OCC workgroups per CU, a whole number per XCD
-  static const int cus = device_cus();
+  const int cus = device_cus();
   const long grid = (cus / 8) * 8 * C::OCC;
   return run_kernel(GU ? "wgrad_gate_up_long" : "wgrad_down_long", s,
                     [&] { wgrad_long_kernel<C, GU, OutT><<<grid, C::NT, 0, s>>>(g); });

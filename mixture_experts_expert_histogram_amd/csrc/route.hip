@@ -58,7 +58,7 @@ __device__ int block_exclusive_scan_1024(int v, int* sh) {
 // Pass 2 (one workgroup): counts, offsets, per-chunk bases, M-tile tables,
 // the bad-id flag, and the experts ordered by descending count.
 __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int32_t* __restrict__ blk_hist,
-                                                          const int32_t* __restrict__ blk_bad,
+                                                          int32_t* __restrict__ blk_bad,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_prefix,
@@ -122,10 +122,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int32
     }
     expert_order[r] = e;
   }
+  // Slots with an id outside [0,E) go after every valid slot, chunk by chunk
+  // in slot order, so positions [offsets[E], S) hold them and every position
+  // names a real slot and token: blk_bad becomes each chunk's first position.
   if (threadIdx.x == 0) {
-    int bad = 0;
-    for (int b = 0; b < nblk; ++b) bad += blk_bad[b];
-    status[0] = bad;
+    const int valid = base[E - 1] + cnt[E - 1];
+    int run = valid;
+    for (int b = 0; b < nblk; ++b) {
+      const int h = blk_bad[b];
+      blk_bad[b] = run;
+      run += h;
+    }
+    status[0] = run - valid;
   }
 }
 
@@ -134,17 +142,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int32
 // with ballots, and a lane's rank is the number of lower lanes in its group.
 // Waves of one round are ordered by wave index, rounds by round index, chunks
 // by the bases from pass 2 — so every expert receives its slots in
-// ascending slot order.
+// ascending slot order.  Slots with a bad id are grouped the same way under
+// the key E and fill the positions after the valid ones (inv_pos -1, routing
+// weight 0, their own token), so every position in [0, S) is written once.
 __global__ __launch_bounds__(ROUTE_THREADS) void route_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ w, int S, int K, int E,
-    const int32_t* __restrict__ blk_base, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ inv_pos,
-    int32_t* __restrict__ tok_of_pos, float* __restrict__ w_of_pos) {
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ blk_bad_base,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ inv_pos, int32_t* __restrict__ tok_of_pos,
+    float* __restrict__ w_of_pos) {
   constexpr int NW = ROUTE_THREADS / 64;
-  __shared__ int running[MAX_E];
-  __shared__ int wcnt[NW][MAX_E];
+  __shared__ int running[MAX_E + 1];
+  __shared__ int wcnt[NW][MAX_E + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += ROUTE_THREADS) {
-    running[e] = blk_base[(size_t)blockIdx.x * E + e];
+  for (int e = tid; e <= E; e += ROUTE_THREADS) {
+    running[e] = e < E ? blk_base[(size_t)blockIdx.x * E + e] : blk_bad_base[blockIdx.x];
 #pragma unroll
     for (int v = 0; v < NW; ++v) wcnt[v][e] = 0;
   }
@@ -152,17 +163,14 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_scatter_kernel(
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < ROUTE_CHUNK / ROUTE_THREADS; ++r) {
     const int s = blockIdx.x * ROUTE_CHUNK + r * ROUTE_THREADS + tid;
-    int e = -1;
+    int e = -1;   // grouping key: the expert id, E for a bad id, -1 past the end
     if (s < S) {
       e = ids[s];
-      if ((unsigned)e >= (unsigned)E) {
-        inv_pos[s] = -1;
-        e = -1;
-      }
+      if ((unsigned)e >= (unsigned)E) e = E;
     }
     uint64_t peers = 0;
     uint64_t todo = __ballot(e >= 0);
-    while (todo) {                       // wave-uniform loop over distinct ids
+    while (todo) {                       // wave-uniform loop over distinct keys
       const int leader = __ffsll((unsigned long long)todo) - 1;
       const int le = __shfl(e, leader);
       const uint64_t m = __ballot(e == le);
@@ -176,12 +184,13 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_scatter_kernel(
       int pos = running[e] + rank;
       for (int v = 0; v < wave; ++v) pos += wcnt[v][e];
       sorted_slot[pos] = s;
-      inv_pos[s] = pos;
       tok_of_pos[pos] = s / K;
-      w_of_pos[pos] = w ? w[s] : 0.f;
+      const bool ok = e < E;
+      inv_pos[s] = ok ? pos : -1;
+      w_of_pos[pos] = (ok && w) ? w[s] : 0.f;
     }
     __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += ROUTE_THREADS) {
+    for (int e2 = tid; e2 <= E; e2 += ROUTE_THREADS) {
       int add = 0;
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
@@ -305,8 +314,9 @@ hipError_t launch_route(const int32_t* ids, const float* w, int S, int K, int E,
   });
   if (err != hipSuccess) return err;
   return run_kernel("route_scatter", stream, [&] {
-    route_scatter_kernel<<<nblk, ROUTE_THREADS, 0, stream>>>(ids, w, S, K, E, rs.blk_hist, rs.sorted_slot,
-                                                             rs.inv_pos, rs.tok_of_pos, rs.w_of_pos);
+    route_scatter_kernel<<<nblk, ROUTE_THREADS, 0, stream>>>(ids, w, S, K, E, rs.blk_hist, rs.blk_bad,
+                                                             rs.sorted_slot, rs.inv_pos, rs.tok_of_pos,
+                                                             rs.w_of_pos);
   });
 }
 

@@ -2,16 +2,32 @@
 
 Bar for floating-point outputs (per tensor): relative Frobenius error
 ||gpu - ref|| / ||ref|| <= 1e-2 and max |gpu - ref| <= 3e-2 * rms(ref).
-Integer routing outputs must be equal.
+Integer routing outputs must be equal.  out, d_hidden, d_topk_weights and
+the stacked weight gradients are held to exactly this bar.
 
-bf16 floor.  In a bf16 workload every GEMM rounds its activation-side
-operand (a, dZ, w*a) to bf16 for the matrix cores, and bf16 outputs are
-rounded once more when stored: the store alone puts up to 2^-8 of an
-element's own magnitude into its error, whatever the implementation, and on
-heavy-tailed tensors (max |ref| above ~8 rms, e.g. the weight gradient of an
-expert with ~100 tokens) that can exceed 3e-2 * rms.  For bf16 workloads the max-abs term is therefore checked beyond
-that floor: |gpu - ref| <= 3e-2 * rms(ref) + 2^-8 * |ref| elementwise.  The
-relative Frobenius bound is unchanged, and fp32 workloads use the plain bar.
+Every check records its plain figures (rel-Frobenius and max|gpu-ref|/rms),
+and the test session prints the worst of them per tensor kind, so the
+margin to the bar is visible whether or not a floor applied.
+
+Floors apply to bf16-stored weight gradients only:
+* the weight-gradient block of a single expert (its dW_gate, dW_up or
+  dW_down checked on its own scale): each such block is a parameter tensor
+  of its own, stored in bf16, whose elements are sums over the expert's c
+  slots of products in which the activation-side factor was rounded to bf16
+  for the matrix cores (bf16 floor, or the slot floor below);
+* the stacked weight gradients when stored in bf16: the bf16 floor alone.
+  Reading: the bar measures the computation, and rounding the exact result
+  to the storage type is not part of it.  On heavy-tailed gradients (max
+  |ref| above ~8 rms) the correctly rounded oracle value itself misses
+  3e-2 * rms at its largest element, so no bf16-storing implementation can
+  meet the plain max-abs term there (tests/test_parity_bar.py shows it on
+  the ragged clamped-GLU case).  fp32-stored gradients take the plain bar.
+
+bf16 floor.  A bf16 store puts up to 2^-8 of an element's own magnitude
+into its error, whatever the implementation, and on a heavy-tailed block
+(max |ref| above ~8 rms, e.g. the gradient of an expert with ~100 tokens)
+that exceeds 3e-2 * rms.  The max-abs term of such a block is checked beyond
+that floor: |gpu - ref| <= 3e-2 * rms(ref) + 2^-8 * |ref| elementwise.
 
 Slot floor (weight gradients of bf16 workloads).  An expert's weight
 gradient is a sum over its c slots of outer products p_s q_s^T (dZ_s with
@@ -27,6 +43,7 @@ beyond 2^-8 |ref| + 2^-8 min(A, 4B).  With one slot the block is a rank-one
 matrix whose largest entries reach 30-60 rms, and the two roundings alone
 exceed the plain bf16 floor by up to ~0.1 rms.
 """
+import os
 import numpy as np
 import torch
 
@@ -52,14 +69,27 @@ BF16_HALF_ULP = 2.0 ** -8   # |bf16(x) - x| <= 2^-8 |x| under round-to-nearest-e
 SLOT_SIGMAS = 4.0           # B multiplier of the statistical operand-rounding bound (docstring)
 
 
-def assert_parity(gpu, ref, name, rel_tol=REL_TOL, max_tol=MAX_TOL, stored_bf16=False):
-    """The bar above.  stored_bf16: the bf16 floor of the module docstring
-    applies (bf16 workloads); the max-abs check then allows 2^-8 |ref| per
-    element beyond 3e-2 * rms."""
+# (kind, label, rel-Frobenius, max|gpu-ref|/rms, floor) of every check this
+# session; printed per kind at the end of the run (tests/conftest.py).
+RECORDS = []
+
+
+def record(kind, label, rel, mx, rms, floor):
+    RECORDS.append((kind, label, float(rel), float(mx / rms) if rms > 0 else 0.0, floor))
+    if os.environ.get("MOE_PARITY_VERBOSE"):
+        print(f"[parity] {kind:16s} {label}: rel-Frobenius {rel:.2e}, max-abs/rms {mx / max(rms, 1e-300):.2e}"
+              f"{'' if floor == 'none' else ' (floor: ' + floor + ')'}", flush=True)
+
+
+def assert_parity(gpu, ref, name, rel_tol=REL_TOL, max_tol=MAX_TOL, stored_bf16=False, kind=None):
+    """The bar above.  stored_bf16 (a single expert's bf16 weight-gradient
+    block only): the bf16 floor of the module docstring; the max-abs check
+    then allows 2^-8 |ref| per element beyond 3e-2 * rms."""
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
     rel, mx, rms = parity_stats(g, r)
+    record(kind or name, name, rel, mx, rms, "bf16 store" if stored_bf16 else "none")
     if rms == 0:
         assert np.all(g == 0), f"{name}: expected exact zeros"
         return rel
@@ -81,14 +111,16 @@ def slot_floor(P, Q):
     return BF16_HALF_ULP * np.minimum(A, SLOT_SIGMAS * B)
 
 
-def assert_parity_slots(gpu, ref, P, Q, name, rel_tol=REL_TOL, max_tol=MAX_TOL):
-    """The bar for a bf16 weight-gradient block ref = sum_s P[s]^T Q[s]:
-    rel-Frobenius <= rel_tol, and |gpu - ref| <= max_tol * rms(ref) beyond the
-    store rounding 2^-8 |ref| and the operand roundings 2^-8 min(A, 4B)."""
+def assert_parity_slots(gpu, ref, P, Q, name, rel_tol=REL_TOL, max_tol=MAX_TOL, kind="dW expert block"):
+    """The bar for a bf16 weight-gradient block ref = sum_s P[s]^T Q[s] of
+    one expert: rel-Frobenius <= rel_tol, and |gpu - ref| <= max_tol * rms(ref)
+    beyond the store rounding 2^-8 |ref| and the operand roundings
+    2^-8 min(A, 4B)."""
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
     rel, mx, rms = parity_stats(g, r)
+    record(kind, name, rel, mx, rms, "slot")
     if rms == 0:
         assert np.all(g == 0), f"{name}: expected exact zeros"
         return rel

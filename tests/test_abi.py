@@ -46,7 +46,7 @@ def test_workspace_sizes_cover_the_buffers():
 def _call_fwd(d, ptr=16, ws_bytes=1 << 40):
     lib = moe.library()
     p = ctypes.c_void_p(ptr)
-    return lib.moe_fwd(ctypes.byref(d), p, p, p, p, p, p, None, p, ws_bytes, None)
+    return lib.moe_fwd(ctypes.byref(d), p, p, p, p, p, p, None, 0, p, ws_bytes, None)
 
 
 def test_argument_errors_before_launch():
@@ -56,7 +56,7 @@ def test_argument_errors_before_launch():
     assert _call_fwd(good, ptr=8) == _lib.MOE_ERR_INVALID_ARG
     # null required pointer
     p = ctypes.c_void_p(16)
-    assert lib.moe_fwd(ctypes.byref(good), None, p, p, p, p, p, None, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd(ctypes.byref(good), None, p, p, p, p, p, None, 0, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
     # workspace too small
     assert _call_fwd(good, ws_bytes=100) == _lib.MOE_ERR_WORKSPACE
     # unsupported shapes
@@ -70,7 +70,7 @@ def test_argument_errors_before_launch():
     d = moe.make_desc(64, 128, 128, 8, 2)
     d.dtype = 7
     assert _call_fwd(d) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_fwd(None, p, p, p, p, p, p, None, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd(None, p, p, p, p, p, p, None, 0, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
     # (T = 0 passes these checks and then clears the status word on the device:
     # covered by the GPU tests)
 
@@ -80,8 +80,8 @@ def test_bwd_argument_errors():
     d = moe.make_desc(64, 128, 128, 8, 2)
     p = ctypes.c_void_p(16)
     args = [p] * 11
-    assert lib.moe_bwd(ctypes.byref(d), *args[:6], None, *args[6:10], p, 100, None) == _lib.MOE_ERR_WORKSPACE
-    assert lib.moe_bwd(ctypes.byref(d), *args[:6], None, p, p, None, p, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_bwd(ctypes.byref(d), *args[:6], None, 0, *args[6:10], p, 100, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_bwd(ctypes.byref(d), *args[:6], None, 0, p, p, None, p, p, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
 
 
 def test_route_and_status_argument_errors():
@@ -106,9 +106,9 @@ def test_router_argument_errors():
     assert lib.moe_router(ctypes.byref(d), ctypes.c_void_p(8), p, p, None, None, None, None, p, big,
                           None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_router(ctypes.byref(d), p, p, p, None, None, None, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
-    assert lib.moe_fwd_logits(ctypes.byref(d), p, None, p, p, p, p, p, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_fwd_logits(ctypes.byref(d9), p, p, p, p, p, p, p, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_fwd_logits(ctypes.byref(d), p, p, p, p, p, p, p, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_fwd_logits(ctypes.byref(d), p, None, p, p, p, p, p, None, 0, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd_logits(ctypes.byref(d9), p, p, p, p, p, p, p, None, 0, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd_logits(ctypes.byref(d), p, p, p, p, p, p, p, None, 0, p, 10, None) == _lib.MOE_ERR_WORKSPACE
     assert lib.moe_router_bwd(ctypes.byref(d), p, p, None, p, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_router_bwd(ctypes.byref(d), p, p, p, ctypes.c_void_p(4), None) == _lib.MOE_ERR_INVALID_ARG
 
@@ -118,9 +118,29 @@ def test_separate_weight_argument_errors():
     p = ctypes.c_void_p(16)
     d = moe.make_desc(64, 8, 8, 8, 2)
     big = 1 << 30
-    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, None, p, p, None, p, big, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, p, 10, None) == _lib.MOE_ERR_WORKSPACE
-    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, p, p, p, None, p, p, big,
+    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, None, p, p, None, 0, p, big, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, 0, p, 10, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, 0, p, p, p, None, p, p, big,
                            None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, p, p, p, p, p, p, 10,
+    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, None, 0, p, p, p, p, p, p, 10,
+                           None) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_saved_buffer_size_is_checked():
+    """A `saved` buffer smaller than moe_workspace_size's saved_bytes is
+    rejected before any launch, by the forward that fills it and by the
+    backward that reads it."""
+    lib = moe.library()
+    d = moe.make_desc(64, 128, 128, 8, 2)
+    _, _, sbytes = moe.workspace_size(d)
+    p = ctypes.c_void_p(16)
+    big = 1 << 40
+    assert lib.moe_fwd(ctypes.byref(d), p, p, p, p, p, p, p, sbytes - 16, p, big, None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_fwd_logits(ctypes.byref(d), p, p, p, p, p, p, p, p, sbytes - 16, p, big,
+                              None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_fwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, p, sbytes - 16, p, big,
+                           None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_bwd(ctypes.byref(d), p, p, p, p, p, p, p, sbytes - 16, p, p, p, p, p, big,
+                       None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_bwd_sep(ctypes.byref(d), p, p, p, p, p, p, p, p, sbytes - 16, p, p, p, p, p, p, big,
                            None) == _lib.MOE_ERR_WORKSPACE

@@ -38,10 +38,34 @@ def test_weight_gradient_split_covers_every_expert(grad_bytes):
         assert m[name + "_hot"][1] == pytest.approx(per_flop * counts[~small & ~long_].sum() * H * I)
         assert m[name + "_long"][1] == pytest.approx(per_flop * counts[long_].sum() * H * I)
         # every expert's gradient is written once, by exactly one of the kernels,
-        # and the operand rows are read once in total
+        # and the hidden / output-gradient rows are read once in total; the
+        # per-slot intermediates (dZ, w*a) are not algorithmic bytes
         dw = (2 if name == "wgrad_gate_up" else 1) * E * H * I * grad_bytes
-        act = S * (2 * I if name == "wgrad_gate_up" else I) * 2
-        assert sum(p[0] for p in parts) - dw == pytest.approx(wl.T * H * 2 + act)
+        assert sum(p[0] for p in parts) - dw == pytest.approx(wl.T * H * 2)
+
+
+def test_projection_bytes_are_weights_and_layer_inputs():
+    """The projections and their input gradients are charged the weights of
+    the experts with slots plus the layer's own input rows, nothing else."""
+    wl = WORKLOADS["gptoss"]
+    counts = np.zeros(wl.E, dtype=np.int64)
+    counts[:3] = [wl.S - 2, 1, 1]
+    m = bench.kernel_model(wl, counts, 2)
+    H, I, T = wl.H, wl.I, wl.T
+    assert m["gate_up_glu"][0] == 3 * 2 * I * H * 2 + T * H * 2
+    assert m["down_weighted"][0] == 3 * H * I * 2
+    assert m["down_dgrad_glu_bwd"][0] == 3 * H * I * 2 + T * H * 2
+    assert m["gate_up_dgrad"][0] == 3 * 2 * I * H * 2
+    assert bench.roofline_for("gate_up_glu", 1.0, m)["bound"] == "mfma"   # 3 experts' weights, 16384 slots
+    spread = bench.kernel_model(wl, np.full(wl.E, wl.S // wl.E, dtype=np.int64), 2)
+    rf = bench.roofline_for("gate_up_glu", 1.0, spread)
+    assert rf["bound"] == "hbm"            # every expert's weights for ~128 slots each: weight-stream bound
+    assert rf["achieved"] == pytest.approx((wl.E * 2 * I * H * 2 + T * H * 2) / 1e-3 / 1e9, rel=1e-3)
+    zipf = WORKLOADS["zipf"]
+    zc = np.full(zipf.E, zipf.S // zipf.E, dtype=np.int64)
+    mz = bench.kernel_model(zipf, zc, 2)
+    rz = bench.roofline_for("gate_up_glu", 2.0, mz)
+    assert rz["bound"] == "mfma" and rz["achieved"] == pytest.approx(4.0 * zipf.S * H * I / 2e-3 / 1e12, rel=1e-3)
 
 
 def test_no_hot_entry_without_hot_experts():

@@ -41,28 +41,59 @@ def check_weight_grads(dgu, dd, r_dgu, r_dd, counts, layout, experts=None, bf16_
             assert np.all(g_gu == 0) and np.all(g_d == 0), f"expert {e} has no slots but nonzero dW"
             continue
         for half, (g, r) in zip(["gate", "up"], zip(gate_up_halves(g_gu, layout), gate_up_halves(r_dgu[e], layout))):
-            assert_parity(g, r, f"dW_{half}[{e}]", stored_bf16=bf)
-        assert_parity(g_d, r_dd[e], f"dW_down[{e}]", stored_bf16=bf)
+            assert_parity(g, r, f"dW_{half}[{e}]", stored_bf16=bf, kind="dW expert block")
+        assert_parity(g_d, r_dd[e], f"dW_down[{e}]", stored_bf16=bf, kind="dW expert block")
 
 
-def run_and_compare(inp, save=True, grad_dtype=None):
+def poisoned_buffers(wl, grad_dtype, dev="cuda"):
+    """Workspaces, saved buffer and outputs of a fwd + bwd call, every byte
+    0xFF (NaN for floats, -1 for integers), so an element a kernel fails to
+    write, or a table it reads before writing, shows in the results."""
+    desc = moe.make_desc(wl.T, wl.H, wl.I, wl.E, wl.K, wl.dtype, wl.act, wl.layout, wl.limit, wl.alpha,
+                         grad_dtype or wl.dtype)
+    fws, bws, sbytes = moe.workspace_size(desc)
+    ff = lambda n: torch.full((max(n, 256),), 0xFF, dtype=torch.uint8, device=dev)
+    adt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    gdt = torch.float32 if (grad_dtype or wl.dtype) == "fp32" else torch.bfloat16
+    nan = lambda shape, dt: torch.full(shape, float("nan"), dtype=dt, device=dev)
+    grads = (nan((wl.T, wl.H), adt), nan((wl.T, wl.K), torch.float32), nan((wl.E, 2 * wl.I, wl.H), gdt),
+             nan((wl.E, wl.H, wl.I), gdt))
+    return dict(ws_f=ff(fws), ws_b=ff(bws), saved=ff(sbytes), out=nan((wl.T, wl.H), adt), grads=grads)
+
+
+def run_gpu(inp, save=True, grad_dtype=None, poison=False, ids=None, expect_status=0):
+    """moe_fwd then moe_bwd on device copies of the inputs (ids: override the
+    device topk_ids); returns (out, d_hidden, d_topk_weights, dW_gate_up, dW_down)."""
     wl = inp.wl
     d = device_inputs(inp)
+    if ids is not None:
+        d["topk_ids"] = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     kw = dict(act=wl.act, layout=wl.layout, limit=wl.limit, alpha=wl.alpha)
+    bufs = poisoned_buffers(wl, grad_dtype) if poison else {}
     out, saved, ws = moe.fwd(d["hidden"], d["topk_ids"], d["topk_weights"], d["w_gate_up"], d["w_down"],
-                             save=save, **kw)
+                             save=save, ws=bufs.get("ws_f"), out=bufs.get("out"),
+                             saved=bufs.get("saved") if save else None, **kw)
     dh, dw, dgu, dd, ws2 = moe.bwd(d["hidden"], d["topk_ids"], d["topk_weights"], d["w_gate_up"], d["w_down"],
-                                   d["d_out"], saved=saved, grad_dtype=grad_dtype, **kw)
+                                   d["d_out"], saved=saved, grad_dtype=grad_dtype, ws=bufs.get("ws_b"),
+                                   grads=bufs.get("grads"), **kw)
     torch.cuda.synchronize()
-    assert moe.check_device_status(ws) == 0 and moe.check_device_status(ws2) == 0
+    assert moe.check_device_status(ws) == expect_status and moe.check_device_status(ws2) == expect_status
+    return out, dh, dw, dgu, dd
+
+
+def run_and_compare(inp, save=True, grad_dtype=None, poison=False):
+    wl = inp.wl
+    out, dh, dw, dgu, dd = run_gpu(inp, save, grad_dtype, poison)
     ref_out, (r_dx, r_dw, r_dgu, r_dd) = oracle_fwd_bwd(inp)
     bf = wl.dtype == "bf16"
-    assert_parity(host(out), ref_out, "out", stored_bf16=bf)
-    assert_parity(host(dh), r_dx, "d_hidden", stored_bf16=bf)
-    assert_parity(host(dw), r_dw, "d_topk_weights", stored_bf16=bf)
-    # stacked weight gradients: relative Frobenius error over all experts
-    assert_parity(host(dgu), r_dgu, "d_w_gate_up", max_tol=np.inf)
-    assert_parity(host(dd), r_dd, "d_w_down", max_tol=np.inf)
+    assert_parity(host(out), ref_out, "out", kind="out")
+    assert_parity(host(dh), r_dx, "d_hidden", kind="d_hidden")
+    assert_parity(host(dw), r_dw, "d_topk_weights", kind="d_topk_weights")
+    # stacked weight gradients (all experts as one tensor): the plain bar, with
+    # only the bf16 store's half-ulp allowed when they are stored in bf16
+    g16 = dgu.dtype == torch.bfloat16
+    assert_parity(host(dgu), r_dgu, "d_w_gate_up", kind="dW stacked", stored_bf16=g16)
+    assert_parity(host(dd), r_dd, "d_w_down", kind="dW stacked", stored_bf16=g16)
     check_weight_grads(dgu, dd, r_dgu, r_dd, np.bincount(inp.topk_ids.ravel(), minlength=wl.E), wl.layout,
                        bf16_workload=bf)
     return out, dh, dw, dgu, dd
@@ -116,9 +147,11 @@ def test_route_bad_id_sets_flag():
     np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(f[good], minlength=8))
     ipn = ip.cpu().numpy()
     assert ipn[21] == -1 and ipn[100] == -1
-    # the good slots keep their stable order
+    # the good slots keep their stable order; the bad ones follow, in slot order
     order = np.argsort(np.where(good, f, 99), kind="stable")[:198]
     np.testing.assert_array_equal(ss.cpu().numpy()[:198], order)
+    np.testing.assert_array_equal(ss.cpu().numpy()[198:], [21, 100])
+    assert offsets.cpu().numpy()[-1] == 198
 
 
 # ------------------------------------------------------------------ fwd + bwd
@@ -219,3 +252,47 @@ def test_weight_grad_expert_sizes(grad_dtype):
     ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
     inp = small_inputs(T, H, I, E, K, "bf16", "clamped", "interleaved", seed=31, ids=ids)
     run_and_compare(inp, grad_dtype=grad_dtype)
+
+
+@pytest.mark.parametrize("save", [True, False])
+def test_poisoned_buffers_ragged(save):
+    """Workspaces, saved buffer and every output start as 0xFF bytes (NaN);
+    a ragged multi-tile case must still match the oracle everywhere."""
+    T, H, I, E, K = 300, 328, 200, 6, 3
+    inp = small_inputs(T, H, I, E, K, "bf16", "clamped", "interleaved", seed=9, ids=skewed_ids(T, K, E, 9))
+    run_and_compare(inp, save=save, grad_dtype="bf16", poison=True)
+
+
+@pytest.mark.parametrize("save", [True, False])
+def test_bad_expert_ids_are_dropped(save):
+    """Ids outside [0, E) (E, E + 100 and -1): the device flags them, nothing
+    outside the caller's buffers is touched (the backward gathers rows for
+    every position, including the bad slots placed last), and every output
+    equals the oracle's for the same inputs with those slots' routing weight
+    set to zero, except d_topk_weights of a bad slot, which is 0.  Buffers
+    start as NaN so a skipped element shows."""
+    T, H, I, E, K = 300, 328, 200, 6, 3
+    inp = small_inputs(T, H, I, E, K, "bf16", "swiglu", "concat", seed=11, ids=skewed_ids(T, K, E, 11))
+    bad_ids = inp.topk_ids.copy()
+    bad = [(5, 1, E), (77, 0, -1), (150, 2, E + 100), (299, 2, E)]
+    for t, k, v in bad:
+        bad_ids[t, k] = v
+    out, dh, dw, dgu, dd = run_gpu(inp, save=save, grad_dtype="bf16", poison=True, ids=bad_ids,
+                                   expect_status=moe.MOE_ERR_BAD_EXPERT_ID)
+    # the oracle's inputs: bad slots on expert 0 with weight 0
+    for t, k, _ in bad:
+        inp.topk_ids[t, k] = 0
+        inp.topk_weights[t, k] = 0.0
+    ref_out, (r_dx, r_dw, r_dgu, r_dd) = oracle_fwd_bwd(inp)
+    assert_parity(host(out), ref_out, "out (bad ids dropped)", kind="out")
+    assert_parity(host(dh), r_dx, "d_hidden (bad ids dropped)", kind="d_hidden")
+    g_dw = host(dw)
+    keep = np.ones((T, K), bool)
+    for t, k, _ in bad:
+        keep[t, k] = False
+        assert g_dw[t, k] == 0.0
+    assert_parity(g_dw[keep], r_dw[keep], "d_topk_weights (bad ids dropped)", kind="d_topk_weights")
+    assert_parity(host(dgu), r_dgu, "d_w_gate_up (bad ids dropped)", kind="dW stacked", stored_bf16=True)
+    assert_parity(host(dd), r_dd, "d_w_down (bad ids dropped)", kind="dW stacked", stored_bf16=True)
+    counts = np.bincount(bad_ids.ravel()[(bad_ids.ravel() >= 0) & (bad_ids.ravel() < E)], minlength=E)
+    check_weight_grads(dgu, dd, r_dgu, r_dd, counts, "concat")

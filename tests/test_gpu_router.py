@@ -103,7 +103,7 @@ def test_fwd_from_logits_equals_fwd_on_router_output(act, layout):
     assert torch.equal(out1, out2)
     r_ids, r_w = oracle.router(lg, K)
     ref = oracle.forward(inp.hidden, r_ids, r_w, oracle.expert_accessor(inp.w_gate_up, inp.w_down), E, act, layout)
-    assert_parity(host(out1), ref, "out from logits", stored_bf16=True)
+    assert_parity(host(out1), ref, "out from logits", kind="out")
 
 
 @pytest.mark.parametrize("T,E,K", [(500, 128, 4), (64, 1024, 64), (3, 8, 8)])

@@ -61,9 +61,9 @@ def check_separate(inp, act, layout, dtype, grad_dtype, save):
     assert moe.check_device_status(ws) == 0 and moe.check_device_status(ws2) == 0
     ref_out, (r_dx, r_dw, r_dgu, r_dd) = oracle_fwd_bwd(inp)
     bf = dtype == "bf16"
-    assert_parity(host(out), ref_out, "out", stored_bf16=bf)
-    assert_parity(host(dh), r_dx, "d_hidden", stored_bf16=bf)
-    assert_parity(host(dw), r_dw, "d_topk_weights", stored_bf16=bf)
+    assert_parity(host(out), ref_out, "out (separate weights)", kind="out")
+    assert_parity(host(dh), r_dx, "d_hidden (separate weights)", kind="d_hidden")
+    assert_parity(host(dw), r_dw, "d_topk_weights (separate weights)", kind="d_topk_weights")
     # gate / up gradients as one concatenated block per expert, checked per expert and half
     r_cat = np.stack([np.concatenate(gate_up_halves(r_dgu[e], layout), axis=0) for e in range(E)])
     got_cat = torch.cat([dg, du], dim=1)
