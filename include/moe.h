@@ -223,6 +223,29 @@ moe_status_t moe_bwd_sep(const moe_desc_t* desc, const void* hidden,
                          void* d_w_up, void* d_w_down, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* Forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * computation, outputs, `saved` / `saved_bytes` and errors as moe_fwd, with
+ * the workspace taken from an array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on (part of its code object, kept until
+ * the process ends); the call allocates nothing.
+ *   - Shapes whose moe_fwd workspace (moe_workspace_size's fwd_ws) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before any device
+ *     call (for H = I = 2880, E = 128, K = 4: up to about 3800 slots).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     a GPU (other streams, other threads) race and must be ordered by the
+ *     caller.  Nothing in the array needs to start at zero.
+ *   - bad_ids (device int32, nullable) receives the number of slots with an
+ *     id outside [0,E) (the status moe_check_device_status reports for
+ *     moe_fwd's workspace). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_fwd_noalloc(const moe_desc_t* desc, const void* hidden,
+                             const int32_t* topk_ids,
+                             const float* topk_weights, const void* w_gate_up,
+                             const void* w_down, void* out, void* saved,
+                             size_t saved_bytes, int32_t* bad_ids,
+                             hipStream_t stream);
+
 /* Synchronises `stream` and reports MOE_ERR_BAD_EXPERT_ID if the last
  * routing done in `ws` met an id outside [0,E), else MOE_OK. */
 moe_status_t moe_check_device_status(const void* ws, hipStream_t stream);

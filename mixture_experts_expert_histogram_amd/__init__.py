@@ -6,7 +6,8 @@ the library in-tree.
 """
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, MOE_ERR_BAD_EXPERT_ID, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
-    MoeDesc, MoeError, bwd, bwd_sep, check_device_status, empty_workspace, fwd, fwd_logits, fwd_sep, library,
+    NOALLOC_SCRATCH_BYTES, MoeDesc, MoeError, bwd, bwd_sep, check_device_status, empty_workspace, fwd, fwd_logits,
+    fwd_noalloc, fwd_sep, library,
     make_desc, route, route_workspace_size, router, router_bwd, status_str, timing_disable, timing_enable,
     timing_read, workspace_size,
 )

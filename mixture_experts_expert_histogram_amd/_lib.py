@@ -20,7 +20,10 @@ MOE_GU_CONCAT, MOE_GU_INTERLEAVED = 0, 1
 
 EXPORTED = ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_router", "moe_fwd",
             "moe_fwd_logits", "moe_fwd_sep", "moe_bwd", "moe_bwd_sep", "moe_router_bwd", "moe_check_device_status",
-            "moe_status_str", "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]
+            "moe_status_str", "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_fwd_noalloc"]
+
+# Size of the library's per-GPU scratch array behind moe_fwd_noalloc (moe.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeDesc(ctypes.Structure):
@@ -66,6 +69,7 @@ def library() -> ctypes.CDLL:
     lib.moe_fwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.moe_bwd_sep.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_fwd_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.moe_check_device_status.argtypes = [vp, vp]
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -74,7 +78,8 @@ def library() -> ctypes.CDLL:
     lib.moe_timing_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     for name in ["moe_workspace_size", "moe_route_workspace_size", "moe_route", "moe_router", "moe_fwd",
                  "moe_fwd_logits", "moe_fwd_sep", "moe_bwd", "moe_bwd_sep", "moe_router_bwd",
-                 "moe_check_device_status", "moe_timing_enable", "moe_timing_disable", "moe_timing_read"]:
+                 "moe_check_device_status", "moe_timing_enable", "moe_timing_disable", "moe_timing_read",
+                 "moe_fwd_noalloc"]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -263,6 +268,21 @@ def fwd(hidden, topk_ids, topk_weights, w_gate_up, w_down, act="swiglu", layout=
                              _ptr(out), _ptr(saved) if save else None, _nbytes(saved) if save else 0, _ptr(ws),
                              ws.numel(), _stream()), "moe_fwd")
     return out, (saved if save else None), ws
+
+
+def fwd_noalloc(hidden, topk_ids, topk_weights, w_gate_up, w_down, act="swiglu", layout="concat", limit=7.0,
+                alpha=1.702, out=None, saved=None, bad_ids=None):
+    """Forward with the library's own per-GPU scratch as workspace (moe_fwd_noalloc);
+    returns out.  `saved` (optional) receives Z as for fwd(save=True); `bad_ids`
+    (optional int32 device tensor of one element) the number of bad-id slots."""
+    import torch
+    d = _desc_for(hidden, topk_ids, w_gate_up, w_down, act, layout, limit, alpha)
+    ids, w = _ids32(topk_ids), _f32(topk_weights)
+    out = torch.empty_like(hidden) if out is None else out
+    _check(library().moe_fwd_noalloc(ctypes.byref(d), _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w_gate_up),
+                                     _ptr(w_down), _ptr(out), _ptr(saved), _nbytes(saved), _ptr(bad_ids),
+                                     _stream()), "moe_fwd_noalloc")
+    return out
 
 
 def bwd(hidden, topk_ids, topk_weights, w_gate_up, w_down, d_out, saved=None, act="swiglu", layout="concat",

@@ -5,6 +5,7 @@
 
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -422,6 +423,52 @@ moe_status_t moe_bwd_sep(const moe_desc_t* desc, const void* hidden, const int32
   if (!w_up || !d_w_up) return MOE_ERR_INVALID_ARG;
   return bwd_impl(desc, hidden, topk_ids, topk_weights, w_gate, w_up, w_down, d_out, saved, saved_bytes, d_hidden,
                   d_topk_weights, d_w_gate, d_w_up, d_w_down, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------ no-allocation forward
+// The workspace of moe_fwd_noalloc: one array per GPU, part of the library's
+// code object, held until the process ends.  Host code never uses the name
+// `scratch` as an address (on the host it is only a stand-in for the symbol);
+// the device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and is what the kernels receive.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+
+// Device address of the current device's scratch array, or null on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+
+moe_status_t moe_fwd_noalloc(const moe_desc_t* desc, const void* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, const void* w_gate_up, const void* w_down, void* out,
+                             void* saved, size_t saved_bytes, int32_t* bad_ids, hipStream_t stream) {
+  Dims d;
+  moe_status_t st = check_desc(desc, &d);
+  if (st != MOE_OK) return st;
+  if (d.T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARG;
+  if (bad_ids && !aligned16(bad_ids)) return MOE_ERR_INVALID_ARG;
+  // beyond the scratch array: rejected before any device call
+  if (make_layout(d).f_end > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return MOE_ERR_HIP;
+  st = fwd_impl(desc, hidden, topk_ids, topk_weights, nullptr, nullptr, nullptr, w_gate_up, nullptr, w_down, out,
+                saved, saved_bytes, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+  if (st != MOE_OK || !bad_ids) return st;
+  HIP_TRY(launch_copy_i32((const int32_t*)ws, bad_ids, 1, stream));   // the routing status word
+  return MOE_OK;
 }
 
 moe_status_t moe_check_device_status(const void* ws, hipStream_t stream) {

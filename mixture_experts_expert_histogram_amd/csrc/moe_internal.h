@@ -58,6 +58,7 @@ hipError_t launch_combine(int dtype, const float* Yp, const int32_t* inv_pos, in
 hipError_t launch_topkw_reduce(const float* partials, int nparts, const int32_t* inv_pos, int S,
                                float* dw, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t stream);
 
 // ---- grouped GEMMs (gemm.hip)
 struct GemmProblem {

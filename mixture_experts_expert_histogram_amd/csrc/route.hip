@@ -449,6 +449,18 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, l
   if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
+// dst[i] = src[i] for n int32 values (a kernel, so the copy is a plain
+// kernel node under graph capture).
+__global__ __launch_bounds__(64) void copy_i32_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst,
+                                                      int n) {
+  for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
+}
+
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  return run_kernel("copy_i32", stream, [&] { copy_i32_kernel<<<1, 64, 0, stream>>>(src, dst, n); });
+}
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return hipSuccess;
   const long n16 = (long)(bytes / 16);
