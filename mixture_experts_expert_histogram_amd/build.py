@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["route.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["route.hip", "gemm.hip", "gemm_dma.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

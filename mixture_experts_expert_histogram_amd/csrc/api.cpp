@@ -42,7 +42,7 @@ Layout make_layout(const Dims& d) {
   L.status = take(4 * sizeof(int32_t));
   L.counts = take(d.E * sizeof(int32_t));
   L.offsets = take((d.E + 1) * sizeof(int32_t));
-  L.tile_prefix = take(N_TILE_BM * (d.E + 1) * sizeof(int32_t));
+  L.tile_prefix = take(N_TILE_TABLES * (d.E + 1) * sizeof(int32_t));
   L.expert_order = take(d.E * sizeof(int32_t));
   L.blk_hist = take((size_t)d.nblk * d.E * sizeof(int32_t));
   L.blk_bad = take((size_t)d.nblk * sizeof(int32_t));
@@ -83,6 +83,7 @@ RouteState route_state(void* ws, const Layout& L, const Dims& d) {
   rs.tok_of_pos = (int32_t*)(b + L.tok_of_pos);
   rs.w_of_pos = (float*)(b + L.w_of_pos);
   rs.nblk = d.nblk;
+  rs.big_min = 0x7fffffff;   // no large-tile experts unless the GEMM problem allows them
   return rs;
 }
 
@@ -330,6 +331,7 @@ static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const i
     pb.w_up = w_up;
     pb.layout = 0;   // Z columns: gate then up
   }
+  rs.big_min = large_tile_min_slots(pb);
   char* b = (char*)ws;
   void* a = b + L.f_a;
   float* yp = (float*)(b + L.f_y);
@@ -381,6 +383,7 @@ static moe_status_t bwd_impl(const moe_desc_t* desc, const void* hidden, const i
     pb.dw_up = d_w_up;
     pb.layout = 0;   // Z and dZ columns: gate then up
   }
+  rs.big_min = large_tile_min_slots(pb);
   char* b = (char*)ws;
   void* z = b + L.b_z;
   void* dz = b + L.b_dz;

@@ -18,83 +18,13 @@
 // operands contiguous along m/n (the weights in the backward's input
 // gradients, every operand of the weight gradients) are read as 8x8 blocks
 // and transposed in registers before their LDS store.
-#include "moe_internal.h"
+#include "gemm_common.h"
 
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
 
 namespace moe {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// ------------------------------------------------------------------ helpers
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// Two fp32 values rounded to bf16 (nearest, ties to even) and packed, low
-// half first: one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-template <typename T> __device__ __forceinline__ void store_val(T* p, float v);
-template <> __device__ __forceinline__ void store_val<uint16_t>(uint16_t* p, float v) {
-  *p = __builtin_bit_cast(uint16_t, (__bf16)v);
-}
-template <> __device__ __forceinline__ void store_val<float>(float* p, float v) { *p = v; }
-
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
-
-// Gated activation (SwiGLU, or the clamped GLU of the gpt-oss-shaped pages).
-__device__ __forceinline__ float glu_fwd(float g, float u, int act, float L, float al) {
-  if (act == 0) return g * sigmoid_f(g) * u;
-  const float gc = fminf(g, L);
-  const float uc = fminf(fmaxf(u, -L), L);
-  return (uc + 1.f) * gc * sigmoid_f(al * gc);
-}
-// Returns a = phi(g,u) and (dg, du) = phi'(g,u) * da.
-__device__ __forceinline__ float glu_bwd(float g, float u, float da, int act, float L, float al, float& dg,
-                                         float& du) {
-  if (act == 0) {
-    const float s = sigmoid_f(g);
-    const float silu = g * s;
-    dg = da * u * s * (1.f + g * (1.f - s));
-    du = da * silu;
-    return silu * u;
-  }
-  const float gc = fminf(g, L);
-  const float uc = fminf(fmaxf(u, -L), L);
-  const float s = sigmoid_f(al * gc);
-  const float q = gc * s;
-  dg = (g <= L) ? da * (uc + 1.f) * s * (1.f + al * gc * (1.f - s)) : 0.f;
-  du = (u >= -L && u <= L) ? da * q : 0.f;
-  return (uc + 1.f) * q;
-}
-
-// The MFMA is issued with the B fragment first, so it computes the tile
-// transposed: accumulator element (fm, fn, v) of a lane is output row
-// wm*WTM + fm*32 + lane%32 and output column wn*WTN + fn*32 + acc_col4 + v%4,
-// where acc_col4 = 8*(v/4) + 4*(lane/32).  A lane therefore holds 4
-// consecutive columns of one row per register group, and stores are 16 (fp32)
-// or 8 (bf16) bytes wide.
-__device__ __forceinline__ int acc_col4(int vg, int lane) { return (vg << 3) + ((lane >> 5) << 2); }
-
-template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
-template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
-  *(uint2*)p = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
-}
-template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
-  *(float4*)p = make_float4(a, b, c, d);
-}
-// interleaved pairs (g0 u0 g1 u1 g2 u2 g3 u3)
-template <typename T> __device__ __forceinline__ void store4x2(T* p, const float* g, const float* u);
-template <> __device__ __forceinline__ void store4x2<uint16_t>(uint16_t* p, const float* g, const float* u) {
-  *(uint4*)p = make_uint4(pack_bf16(g[0], u[0]), pack_bf16(g[1], u[1]), pack_bf16(g[2], u[2]), pack_bf16(g[3], u[3]));
-}
-template <> __device__ __forceinline__ void store4x2<float>(float* p, const float* g, const float* u) {
-  *(float4*)p = make_float4(g[0], u[0], g[1], u[1]);
-  *(float4*)(p + 4) = make_float4(g[2], u[2], g[3], u[3]);
-}
 
 // ------------------------------------------------------------------ config
 template <typename T, int BM_, int BN_, int BK_, int WM_, int WN_>
@@ -325,9 +255,6 @@ struct NLoader {
   }
 };
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-typedef __attribute__((address_space(3))) char lds_char;
 
 // 32 columns x 16 k of an NLoader tile: lane -> column cb + lane%32,
 // k = kk*16 + 8*(lane/32) + 0..7 (the layout of the K-contiguous fragments).
@@ -565,107 +492,6 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
   }
 }
 
-// ------------------------------------------------------------------ arguments
-struct GArgs {
-  const int32_t* offsets;
-  const int32_t* tile_prefix;   // for this kernel's BM
-  const int32_t* tok_of_pos;
-  const float* w_of_pos;
-  const int32_t* expert_order;
-  const void* A;
-  const void* B;
-  const void* Z;
-  void* out0;
-  void* out1;
-  float* partials;
-  int T, H, I, E, K, S;
-  int act, layout;
-  float limit, alpha;
-  int ntn, ntm, nparts;
-  int big;   // weight grads: experts with more positions than this are split over the XCDs
-  int small_max;   // weight grads: the tiled kernel takes only experts with more positions (-1: all)
-  int hot_min;     // weight grads: experts with more positions go to the long-K kernel (0: none)
-  // Gate/up rows of the weights (gu_*) and of their gradients (dgu_*): row j of
-  // expert e's gate (up) projection starts gu_es*e + gu_rs*j elements after
-  // gu_g (gu_u).  Fused [E,2I,H] concatenated: (W, W + I*H, 2IH, H);
-  // interleaved: (W, W + H, 2IH, 2H); separate [E,I,H] tensors: (Wg, Wu, IH, H).
-  const void* gu_g;
-  const void* gu_u;
-  void* dgu_g;
-  void* dgu_u;
-  long gu_es, gu_rs;
-  int gu_sep;   // separate gate and up tensors (Z and dZ columns then concatenated)
-};
-
-// Row j of expert e's gate (up = 0) or up (up = 1) projection.
-template <typename P>
-__device__ __forceinline__ P* gu_row(P* g0, P* u0, long es, long rs, int e, int up, int j) {
-  return (up ? u0 : g0) + es * e + rs * j;
-}
-
-// Gate/up half and index of column m of Z and dZ [S,2I] (interleaved:
-// columns 2j, 2j+1; otherwise gate columns [0,I), up columns [I,2I)).
-__device__ __forceinline__ void zcol(int m, int I, int layout, int& up, int& j) {
-  up = layout ? (m & 1) : (m >= I);
-  j = layout ? (m >> 1) : m - (up ? I : 0);
-}
-
-constexpr int kRowTileGroup = 8;
-
-// Token-row tiles: (expert, N-tile, M-tile of BM rows), ordered by expert,
-// then by groups of M-tiles, then N-tile, then M-tile, so the M-tiles of one
-// expert that share a weight tile are neighbours.  The grid is sized for the worst case; the actual tile
-// count is read from the routing tables and split into 8 equal contiguous
-// ranges, one per XCD (hardware deals workgroup b to XCD b % 8).  Returns
-// false for a workgroup without a tile.
-template <int BM>
-__device__ __forceinline__ bool row_tile(const GArgs& g, int& e, int& m0, int& rows, int& nt) {
-  const int* tp = g.tile_prefix;
-  const int ntn = g.ntn;
-  const int total = tp[g.E] * ntn;
-  const int per = (total + 7) >> 3;
-  const int b = blockIdx.x, j = b >> 3;
-  if (j >= per) return false;
-  const int t = (b & 7) * per + j;
-  if (t >= total) return false;
-  const int q = t / ntn;
-  int lo = 0, hi = g.E;            // largest e with tp[e] <= q
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tp[mid] <= q) lo = mid; else hi = mid - 1;
-  }
-  e = lo;
-  const int nm = tp[e + 1] - tp[e];
-  // Inside an expert the M-tiles go in groups of kRowTileGroup; a group's
-  // tiles run N-tile by N-tile, M-tile fastest.  The ~64 workgroups an XCD
-  // holds at once then cover an 8x8 block of (M, N) tiles, each token-row
-  // block and each weight tile read by 8 of them; N-tile-major order over a
-  // whole hot expert re-streamed its token rows once per N-tile (Zipf
-  // workload gate_up: 32.5 GB fetched per launch, 20.5 GB grouped).  Experts
-  // with at most kRowTileGroup M-tiles keep the N-major order.
-  const int local = t - tp[e] * ntn;
-  const int gsz = kRowTileGroup * ntn;
-  const int grp = local / gsz;
-  const int rem = local - grp * gsz;
-  const int gm = min(kRowTileGroup, nm - grp * kRowTileGroup);
-  nt = rem / gm;
-  const int mt = grp * kRowTileGroup + (rem - nt * gm);
-  m0 = g.offsets[e] + mt * BM;
-  rows = min(BM, g.offsets[e + 1] - m0);
-  return true;
-}
-
-// Weight-gradient tiles: chunks of CH consecutive tiles are dealt
-// round-robin to the XCDs (experts longest first), so every XCD gets a
-// similar share of long and short experts and a chunk's tiles share operands
-// in one L2.  The j-th tile of this workgroup's XCD, or -1 past the end.
-template <int CH>
-__device__ __forceinline__ int dealt_tile(int j, int total) {
-  const int x = blockIdx.x & 7;
-  const int t = ((j / CH) * 8 + x) * CH + j % CH;
-  return t < total ? t : -1;
-}
-
 #define GEMM_PROLOGUE(C)                                                   \
   using T = typename C::elem;                                              \
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];     \
@@ -721,41 +547,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_kernel(GArgs g) {
   mainloop_rows<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
                    [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
                    (H + C::BK - 1) / C::BK, lds, acc);
-
-  T* a_out = (T*)g.out0;
-  float* z_out = (float*)g.out1;
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
-    if (rl >= rows) continue;
-    const size_t p = (size_t)(m0 + rl);
-#pragma unroll
-    for (int pr = 0; pr < C::FN / 2; ++pr)
-#pragma unroll
-    for (int vg = 0; vg < 4; ++vg) {
-      const int j = j0 + (wn * (C::FN / 2) + pr) * 32 + acc_col4(vg, lane);
-      if (j >= I) continue;
-      float gv[4], uv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gv[i] = acc[fm][2 * pr][vg * 4 + i];
-        uv[i] = acc[fm][2 * pr + 1][vg * 4 + i];
-      }
-      if (WRITE_A)
-        store4<T>(a_out + p * I + j, glu_fwd(gv[0], uv[0], g.act, g.limit, g.alpha),
-                  glu_fwd(gv[1], uv[1], g.act, g.limit, g.alpha), glu_fwd(gv[2], uv[2], g.act, g.limit, g.alpha),
-                  glu_fwd(gv[3], uv[3], g.act, g.limit, g.alpha));
-      if (WRITE_Z) {
-        float* zr = z_out + p * 2 * I;
-        if (layout) {
-          store4x2<float>(zr + 2 * j, gv, uv);
-        } else {
-          store4<float>(zr + j, gv[0], gv[1], gv[2], gv[3]);
-          store4<float>(zr + I + j, uv[0], uv[1], uv[2], uv[3]);
-        }
-      }
-    }
-  }
+  epi_gate_up<C, T, WRITE_A, WRITE_Z>(g, acc, m0, rows, j0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- down fwd
@@ -776,23 +568,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void down_kernel(GArgs g) {
   mainloop_rows<C>(al, bl, [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
                    [](auto& l, int kt, auto set) { l.template load<decltype(set)::value>(kt); },
                    (I + C::BK - 1) / C::BK, lds, acc);
-  float* Y = (float*)g.out0;
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
-    if (rl >= rows) continue;
-    const size_t p = (size_t)(m0 + rl);
-    const float w = g.w_of_pos[p];
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
-        if (n < H)
-          store4<float>(Y + p * H + n, w * acc[fm][fn][vg * 4], w * acc[fm][fn][vg * 4 + 1],
-                        w * acc[fm][fn][vg * 4 + 2], w * acc[fm][fn][vg * 4 + 3]);
-      }
-  }
+  epi_down<C>(g, acc, m0, rows, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- down dgrad
@@ -820,79 +596,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void down_dgrad_kernel(GArgs g) {
   if constexpr (kTwoSets<C>) mainloop<C, false, true>(al, bl, aload, bload, nk, lds, acc);
   else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, nk, lds, acc);
 
-  const float* Z = (const float*)g.Z;
-  T* dZ = (T*)g.out0;
-  T* aw = (T*)g.out1;
-  const int layout = g.layout;
-  float* red = (float*)smem_raw;   // [WN][BM]; the K loop ended with a barrier
-  // Per 32-row group, all of the lane's Z values are loaded first, from
-  // addresses clamped into the tile (rows past the tile's end read its last
-  // row, columns past I the last four), and only the results are
-  // predicated.  Loads issued one register group at a time behind the bounds
-  // test each waited out the HBM latency: 0.84 -> 0.78 ms on the gpt-oss
-  // layer, 4.60 -> 4.00 ms on the Zipf batch.
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
-    float rs = 0.f;
-    const size_t p = (size_t)(m0 + min(rl, rows - 1));
-    const float w = g.w_of_pos[p];
-    const float* zr = Z + p * 2 * I;
-    T* dzr = dZ + p * 2 * I;
-    // interleaved rows: (g, u) pairs, za = columns i, i+1, zb = i+2, i+3;
-    // concatenated rows: za = gate, zb = up, columns i .. i+3
-    float4 za[C::FN][4], zb[C::FN][4];
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int i = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
-        const int ic = i < I ? i : I - 4;   // I is a multiple of 8
-        za[fn][vg] = *(const float4*)(zr + (layout ? 2 * ic : ic));
-        zb[fn][vg] = *(const float4*)(zr + (layout ? 2 * ic + 4 : I + ic));
-      }
-    if (rl < rows) {
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int vg = 0; vg < 4; ++vg) {
-          const int i = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
-          if (i >= I) continue;
-          const float4 z0 = za[fn][vg], z1 = zb[fn][vg];
-          float gv[4], uv[4];
-          if (layout) {
-            gv[0] = z0.x; uv[0] = z0.y; gv[1] = z0.z; uv[1] = z0.w;
-            gv[2] = z1.x; uv[2] = z1.y; gv[3] = z1.z; uv[3] = z1.w;
-          } else {
-            gv[0] = z0.x; gv[1] = z0.y; gv[2] = z0.z; gv[3] = z0.w;
-            uv[0] = z1.x; uv[1] = z1.y; uv[2] = z1.z; uv[3] = z1.w;
-          }
-          float dg[4], du[4], a[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float r = acc[fm][fn][vg * 4 + q];
-            a[q] = glu_bwd(gv[q], uv[q], w * r, g.act, g.limit, g.alpha, dg[q], du[q]);
-            rs += r * a[q];
-          }
-          if (layout) {
-            store4x2<T>(dzr + 2 * i, dg, du);
-          } else {
-            store4<T>(dzr + i, dg[0], dg[1], dg[2], dg[3]);
-            store4<T>(dzr + I + i, du[0], du[1], du[2], du[3]);
-          }
-          store4<T>(aw + p * I + i, w * a[0], w * a[1], w * a[2], w * a[3]);
-        }
-    }
-    // this lane and lane^32 hold the two column halves of the same row
-    rs += __shfl_xor(rs, 32);
-    if (lane < 32) red[wn * C::BM + wm * C::WTM + fm * 32 + lane] = rs;
-  }
-  __syncthreads();
-  for (int r = threadIdx.x; r < rows; r += C::NT) {
-    float s = 0.f;
-    for (int q = 0; q < C::WN; ++q) s += red[q * C::BM + r];
-    g.partials[(size_t)(m0 + r) * g.nparts + nt] = s;
-  }
+  // the K loop ended with a barrier, so LDS is free for the row reduction
+  epi_down_dgrad<C, T>(g, acc, m0, rows, n0, nt, wm, wn, lane, (float*)smem_raw);
 }
 
 // ---------------------------------------------------------------- gate_up dgrad
@@ -925,22 +630,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_up_dgrad_kernel(GArgs g) {
   const int nk = (I2 + C::BK - 1) / C::BK;
   if constexpr (kTwoSets<C>) mainloop<C, false, true>(al, bl, aload, bload, nk, lds, acc);
   else mainloop_pf1<C, false, kNLayout<C>>(al, bl, aload, bload, nk, lds, acc);
-  float* dXp = (float*)g.out0;
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int rl = wm * C::WTM + fm * 32 + (lane & 31);
-    if (rl >= rows) continue;
-    const size_t p = (size_t)(m0 + rl);
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
-        if (n < H)
-          store4<float>(dXp + p * H + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
-                        acc[fm][fn][vg * 4 + 3]);
-      }
-  }
+  epi_gate_up_dgrad<C>(g, acc, m0, rows, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- weight grads
@@ -1792,51 +1482,6 @@ using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
 using CfgWB = Cfg<uint16_t, 128, 128, 64, 2, 4>;
 using CfgWF = Cfg<float, 128, 128, 16, 2, 2>;
 
-static constexpr int bm_index(int bm) { return bm == 32 ? 0 : bm == 64 ? 1 : bm == 128 ? 2 : bm == 256 ? 3 : 4; }
-
-static GArgs base_args(const GemmProblem& pb, int bm) {
-  GArgs g = {};
-  const RouteState& rs = *pb.rs;
-  g.offsets = rs.offsets;
-  g.tile_prefix = rs.tile_prefix + bm_index(bm) * (pb.E + 1);
-  g.tok_of_pos = rs.tok_of_pos;
-  g.w_of_pos = rs.w_of_pos;
-  g.expert_order = rs.expert_order;
-  g.T = pb.T; g.H = pb.H; g.I = pb.I; g.E = pb.E; g.K = pb.K; g.S = pb.S;
-  g.act = pb.act; g.layout = pb.layout; g.limit = pb.limit; g.alpha = pb.alpha;
-  return g;
-}
-
-// The gate/up row view of a weight-shaped tensor (see GArgs).
-static void gu_view(const GemmProblem& pb, const void* fused_or_gate, const void* up, size_t esz, const void*& g0,
-                    const void*& u0) {
-  const size_t IH = (size_t)pb.I * pb.H;
-  g0 = fused_or_gate;
-  if (pb.w_up) u0 = up;
-  else u0 = (const char*)fused_or_gate + (pb.layout ? (size_t)pb.H : IH) * esz;
-}
-static void set_gu(GArgs& g, const GemmProblem& pb, const void* w, void* dw, size_t dw_esz) {
-  const size_t esz = pb.dtype == 0 ? 2 : 4;
-  const long IH = (long)pb.I * pb.H;
-  g.gu_sep = pb.w_up != nullptr;
-  g.gu_es = pb.w_up ? IH : 2 * IH;
-  g.gu_rs = (!pb.w_up && pb.layout) ? 2L * pb.H : pb.H;
-  if (w) gu_view(pb, w, pb.w_up, esz, g.gu_g, g.gu_u);
-  if (dw) {
-    const void *dg, *du;
-    gu_view(pb, dw, pb.dw_up, dw_esz, dg, du);
-    g.dgu_g = (void*)dg;
-    g.dgu_u = (void*)du;
-  }
-}
-
-static int mtiles_upper(int S, int E, int bm) { return (S + bm - 1) / bm + (E < S ? E : S); }
-// Token-row grids: worst-case tile count, rounded up to 8 plus 8 (see row_tile).
-static long row_grid(const GemmProblem& pb, int bm, int ntn) {
-  const long t = (long)mtiles_upper(pb.S, pb.E, bm) * ntn;
-  return ((t + 7) / 8) * 8 + 8;
-}
-
 template <class C, bool A, bool Z>
 static hipError_t gate_up_impl(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
                                hipStream_t s) {
@@ -1856,10 +1501,27 @@ static hipError_t gate_up_dispatch(const GemmProblem& pb, const void* X, const v
   return gate_up_impl<C, false, true>(pb, X, Wgu, a_out, z_out, s);
 }
 
+// With the large-tile engine on, a token-row GEMM runs as two launches: the
+// experts with at least rs->big_min slots in 256 x 256 tiles (gemm_dma.hip),
+// then the others in this engine's 128-row tiles (192-row when experts
+// average 101-176 slots), each over its own tile table.
+static GemmProblem small_experts(const GemmProblem& pb) {
+  GemmProblem p = pb;
+  p.tile_set = 2;
+  return p;
+}
+
 hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
                           hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
   if (pb.dtype != 0) return gate_up_dispatch<CfgF>(pb, X, Wgu, a_out, z_out, s);
+  if (dma_enabled(pb)) {
+    const hipError_t e = dma_gate_up(pb, X, Wgu, a_out, z_out, s);
+    if (e != hipSuccess) return e;
+    const GemmProblem ps = small_experts(pb);
+    return use_bm192(pb) ? gate_up_dispatch<CfgB192>(ps, X, Wgu, a_out, z_out, s)
+                         : gate_up_dispatch<CfgB>(ps, X, Wgu, a_out, z_out, s);
+  }
   if (use_bm256(pb)) return gate_up_dispatch<CfgB256>(pb, X, Wgu, a_out, z_out, s);
   return use_bm192(pb) ? gate_up_dispatch<CfgB192>(pb, X, Wgu, a_out, z_out, s)
                        : gate_up_dispatch<CfgB>(pb, X, Wgu, a_out, z_out, s);
@@ -1877,6 +1539,12 @@ static hipError_t down_impl(const GemmProblem& pb, const void* a, const void* Wd
 hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
   if (pb.dtype != 0) return down_impl<CfgF>(pb, a, Wd, Yp, s);
+  if (dma_enabled(pb)) {
+    const hipError_t e = dma_down(pb, a, Wd, Yp, s);
+    if (e != hipSuccess) return e;
+    const GemmProblem ps = small_experts(pb);
+    return use_bm192(pb) ? down_impl<CfgB192>(ps, a, Wd, Yp, s) : down_impl<CfgB>(ps, a, Wd, Yp, s);
+  }
   if (use_bm256(pb)) return down_impl<CfgB256>(pb, a, Wd, Yp, s);
   return use_bm192(pb) ? down_impl<CfgB192>(pb, a, Wd, Yp, s) : down_impl<CfgB>(pb, a, Wd, Yp, s);
 }
@@ -1902,6 +1570,13 @@ hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* 
   // 0.78 -> 0.71 ms); 256-row tiles for larger experts measured slower here
   // (Zipf batch 3.99 -> 4.04 ms), so those keep 128 rows.
   if (pb.dtype != 0) return down_dgrad_impl<CfgF>(pb, dY, Wd, Z, dZ, aw, partials, s);
+  if (dma_enabled(pb)) {
+    const hipError_t e = dma_down_dgrad(pb, dY, Wd, Z, dZ, aw, partials, *nparts, s);
+    if (e != hipSuccess) return e;
+    const GemmProblem ps = small_experts(pb);
+    return use_bm192(pb) ? down_dgrad_impl<CfgB192>(ps, dY, Wd, Z, dZ, aw, partials, s)
+                         : down_dgrad_impl<CfgB>(ps, dY, Wd, Z, dZ, aw, partials, s);
+  }
   return use_bm192(pb) ? down_dgrad_impl<CfgB192>(pb, dY, Wd, Z, dZ, aw, partials, s)
                        : down_dgrad_impl<CfgB>(pb, dY, Wd, Z, dZ, aw, partials, s);
 }
@@ -1923,6 +1598,13 @@ static hipError_t gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, cons
 hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
   if (pb.S == 0) return hipSuccess;
   if (pb.dtype != 0) return gate_up_dgrad_impl<CfgF>(pb, dZ, Wgu, dXp, s);
+  if (dma_enabled(pb)) {
+    const hipError_t e = dma_gate_up_dgrad(pb, dZ, Wgu, dXp, s);
+    if (e != hipSuccess) return e;
+    const GemmProblem ps = small_experts(pb);
+    return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(ps, dZ, Wgu, dXp, s)
+                         : gate_up_dgrad_impl<CfgB>(ps, dZ, Wgu, dXp, s);
+  }
   if (use_bm256(pb)) return gate_up_dgrad_impl<CfgB256>(pb, dZ, Wgu, dXp, s);
   return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(pb, dZ, Wgu, dXp, s)
                        : gate_up_dgrad_impl<CfgB>(pb, dZ, Wgu, dXp, s);

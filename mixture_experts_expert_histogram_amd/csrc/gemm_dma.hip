@@ -1,0 +1,479 @@
+// Large-tile engine for the token-row GEMMs of experts with many slots.
+//
+// When an expert holds hundreds to tens of thousands of slots its gate_up,
+// down and input-gradient products are dense GEMMs bound by the matrix
+// cores, not by the weight stream.  For those experts this engine computes
+// 256 x 256 tiles on 8 waves (2 x 4, 128 x 64 per wave) of
+// v_mfma_f32_32x32x16_bf16, with both operands moved from global memory
+// straight into LDS by global_load_lds_dwordx4 (no staging registers, no
+// ds_write), through a ring of four LDS stages of BK = 32:
+//
+// * Every step starts with a wait for the wave's own loads of that step
+//   (vmcnt, three steps of loads stay in flight) and a barrier, then refills
+//   the stage the previous step read with the step three ahead, then reads
+//   the fragments of the current stage and runs its MFMAs.
+// * The four stages are four distinct __shared__ arrays, the ring is unrolled
+//   by four and every refill is issued unconditionally (clamped to the last
+//   step), so the compiler's wait insertion can tell the stage being read from
+//   the stages in flight and never drains the ring (one array, or a branch
+//   around a refill, made it wait for every load before each read).
+// * The barrier is a plain s_barrier after an explicit wait (vmcnt(8),
+//   lgkmcnt(0)); __syncthreads() would also wait for every load in flight.
+// * A load writes 64 lanes x 16 bytes to consecutive LDS bytes; the tiles'
+//   XOR swizzles come from permuting which 16 bytes of global memory each
+//   lane reads.
+//
+// Measured on a dense 24576 x 5632 x 2880 bf16 product: 981 TFLOP/s, against
+// 936 with register-staged loads and ds_write (the LDS writes of the staged
+// tiles were the largest cost: 1195 TFLOP/s with them left out) and 1006 for
+// hipBLASLt on the same shape.
+//
+// Operands contiguous along k are [row][32] tiles (64-byte rows, 16-byte
+// chunks XORed with (row / 4) % 4); operands contiguous along m or n (the
+// weights of the input gradients) are [32][128] column halves read with
+// ds_read_b64_tr_b16, like the other engine's.  K must be a multiple of 32.
+#include "gemm_common.h"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) void* lds_vp;
+
+// A pointer made provably wave-uniform (both halves read from lane 0), for
+// the scalar base of a load.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 16 bytes per lane from base + off (base wave-uniform, off a per-lane byte
+// offset below 2^31) to LDS at dst + 16 * lane (dst wave-uniform).
+//
+// Written as one asm block (M0 = LDS address, the one wait state an M0 write
+// needs before an LDS DMA, the load): the compiler's wait insertion then
+// does not track these loads, and the mainloop orders them itself with an
+// explicit vmcnt before every barrier and vmcnt(0) at the end.  Tracked, they
+// made the compiler wait for every load in flight before each transposing
+// LDS read (ds_read_b64_tr_b16 carries no LDS alias information), which
+// drained the ring in every step of the input-gradient kernels.  The load
+// has no output register; the compiler's own vmcnt waits stay correct
+// because vector memory counts complete in order, so untracked loads issued
+// after one of its own only make its waits stricter.  The scalar base with a
+// 32-bit offset keeps one VGPR per load instead of a 64-bit address.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint16_t* dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_vp)dst;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory", "m0");
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct DCfg {
+  using elem = uint16_t;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32, NSTAGE = 4;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK, STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int NBA = BM / 16 / NW, NBB = BN / 16 / NW;   // 1 KB loads per wave and step
+  static constexpr int PER = NBA + NBB;
+  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "whole 1 KB loads per wave");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "column halves of 128");
+};
+using DCfgB = DCfg<256, 256, 2, 4>;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): vmcnt <= n and lgkmcnt = 0.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Element offset of 16-byte chunk `chunk` (0..3) of row `row` in a [row][32]
+// tile: 16 lanes reading one chunk of 16 consecutive rows hit 16 bank groups.
+__device__ __forceinline__ int krow_off(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3); }
+
+// A k-contiguous operand: NB loads per wave per step, load j of wave w holds
+// tile rows (w * NB + j) * 16 .. +16; lane l reads 16 bytes of row
+// 16 b + l / 4, the chunk whose swizzled slot is l % 4.  A load's 16 rows
+// share one scalar base (rows of one 32-row gate or up group).
+template <int NB>
+struct RowSrc {
+  const char* base[NB];
+  uint32_t off[NB];
+  // rowsrc(r, base, off): tile row r (clamped by the caller) starts `off`
+  // bytes after `base`, which is the same for the 16 rows of a load
+  template <class RowSrcFn>
+  __device__ __forceinline__ void init(RowSrcFn rowsrc, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int row = (wave * NB + j) * 16 + (lane >> 2);
+      const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+      const char* b;
+      uint32_t o;
+      rowsrc(row, b, o);
+      base[j] = uniform_ptr(b);
+      off[j] = o + chunk * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, uint16_t* tile, int wave) const {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) lds_dma16(base[j], off[j] + kt * 64, tile + (wave * NB + j) * 512);
+  }
+};
+
+// An operand contiguous along m or n (k rows of columns): the tile is
+// [32 k][COLS] held as COLS / 128 halves of [32][128] (256-byte rows, chunks
+// XORed with 4 * (k % 4)); load b covers half b / 8, k rows 4 (b % 8) .. +4;
+// lane l reads 16 bytes of k row 4 (b % 8) + l / 16.  k rows below ksplit
+// are rows of base0, the others rows k - ksplit of base1 (ksplit a multiple
+// of 32, so a step takes one side); ld elements per row; columns past the
+// valid ones are clamped.
+template <int NB>
+struct ColSrc {
+  const char* b0;
+  const char* b1;
+  uint32_t off[NB];   // bytes from a step's first k row to this lane's 16 bytes
+  uint32_t row_bytes;
+  int ksplit;
+  __device__ __forceinline__ void init(const uint16_t* base0, const uint16_t* base1, long ld, int ksplit_,
+                                       int ncols, int c0, int wave, int lane) {
+    b0 = uniform_ptr(base0);
+    b1 = uniform_ptr(base1);
+    row_bytes = (uint32_t)(ld * 2);
+    ksplit = ksplit_;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int b = wave * NB + j;
+      const int krow = (b & 7) * 4 + (lane >> 4);
+      const int chunk = (lane & 15) ^ ((krow & 3) << 2);
+      const int col = min(c0 + (b >> 3) * 128 + chunk * 8, ncols - 8);
+      off[j] = krow * row_bytes + col * 2;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, uint16_t* tile, int wave) const {
+    const int k0 = kt * 32;
+    const bool lo = k0 < ksplit;
+    const char* b = lo ? b0 : b1;
+    const uint32_t koff = (uint32_t)(lo ? k0 : k0 - ksplit) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) lds_dma16(b, koff + off[j], tile + (wave * NB + j) * 512);
+  }
+};
+
+// 32 columns x 16 k of a [32][128]-half tile (columns from cb), in the
+// fragment layout of the k-contiguous reads: lane -> column cb + lane % 32,
+// k = kk * 16 + 8 (lane / 32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_cols(const uint16_t* tile, int cb, int kk, int lane) {
+  tile += (cb >> 7) * (32 * 128);
+  cb &= 127;
+  const int g = lane >> 4, s = lane & 15;
+  const int col = cb + ((g & 1) << 4) + ((s & 3) << 2);
+  const int chunk = col >> 3, within = (col & 7) * 2;
+  const lds_char* base = (const lds_char*)tile;
+  s16x4_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int krow = kk * 16 + ((g >> 1) << 3) + h * 4 + (s >> 2);
+    r[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + krow * 256 + ((chunk ^ ((krow & 3) << 2)) << 4) + within));
+  }
+  bf16x8_t out;
+  s16x4_t* o = (s16x4_t*)&out;
+  o[0] = r[0];
+  o[1] = r[1];
+  return out;
+}
+
+template <class C>
+struct DFrags {
+  bf16x8_t a[C::FM], b[C::FN];
+};
+
+template <class C, bool A_MN, bool B_MN>
+__device__ __forceinline__ void dma_read(const uint16_t* As, const uint16_t* Bs, int kk, DFrags<C>& f, int wm,
+                                         int wn, int lane) {
+  const int r32 = lane & 31, chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    f.a[i] = A_MN ? frag_cols(As, wm * C::WTM + i * 32, kk, lane)
+                  : *(const bf16x8_t*)(As + krow_off(wm * C::WTM + i * 32 + r32, chunk));
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    f.b[j] = B_MN ? frag_cols(Bs, wn * C::WTN + j * 32, kk, lane)
+                  : *(const bf16x8_t*)(Bs + krow_off(wn * C::WTN + j * 32 + r32, chunk));
+}
+
+template <class C>
+__device__ __forceinline__ void dma_mma(const DFrags<C>& f, f32x16 (&acc)[C::FM][C::FN]) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// Loads of step kt into stage St (A tile, then B tile).
+template <class C, class AS, class BS>
+__device__ __forceinline__ void dma_issue(const AS& as, const BS& bs, int kt, uint16_t* St, int wave) {
+  as.issue(kt, St, wave);
+  bs.issue(kt, St + C::A_ELEMS, wave);
+}
+
+// Step kt on stage Sc; Sp (read by step kt-1) is refilled with step kt+3.
+template <class C, bool A_MN, bool B_MN, class AS, class BS>
+__device__ __forceinline__ void dma_step(const AS& as, const BS& bs, int kt, int last, const uint16_t* Sc,
+                                         uint16_t* Sp, f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn,
+                                         int lane) {
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));   // own loads of step kt landed
+  __builtin_amdgcn_s_barrier();                                          // everyone's; Sp read by all
+  dma_issue<C>(as, bs, min(kt + C::NSTAGE - 1, last), Sp, wave);
+  DFrags<C> f0, f1;
+  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 0, f0, wm, wn, lane);
+  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 1, f1, wm, wn, lane);
+  dma_mma<C>(f0, acc);
+  dma_mma<C>(f1, acc);
+}
+
+// acc = A . B^T over nk steps of 32 k.  S0..S3 are the kernel's four stage
+// arrays (A tile, then B tile).  Ends with every load landed.
+template <class C, bool A_MN, bool B_MN, class AS, class BS>
+__device__ __forceinline__ void dma_mainloop(const AS& as, const BS& bs, int nk, uint16_t* S0, uint16_t* S1,
+                                             uint16_t* S2, uint16_t* S3, f32x16 (&acc)[C::FM][C::FN], int wave,
+                                             int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int last = nk - 1;
+  dma_issue<C>(as, bs, 0, S0, wave);
+  dma_issue<C>(as, bs, min(1, last), S1, wave);
+  dma_issue<C>(as, bs, min(2, last), S2, wave);
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    dma_step<C, A_MN, B_MN>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane);
+    dma_step<C, A_MN, B_MN>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane);
+    dma_step<C, A_MN, B_MN>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane);
+    dma_step<C, A_MN, B_MN>(as, bs, kt + 3, last, S3, S2, acc, wave, wm, wn, lane);
+  }
+  if (kt < nk) dma_step<C, A_MN, B_MN>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane);
+  if (kt + 1 < nk) dma_step<C, A_MN, B_MN>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane);
+  if (kt + 2 < nk) dma_step<C, A_MN, B_MN>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no load may outlive the tile (or the workgroup's LDS)
+}
+
+// Persistent workgroups, one per CU: workgroup b walks tiles b / 8,
+// b / 8 + gridDim / 8, ... of XCD b % 8's contiguous range of the tile table
+// (TILE_LOOP).  The barrier between tiles keeps a tile's first loads out of
+// stages that slower waves may still be reading for the previous one.
+#define TILE_LOOP(C)                                                                          \
+  int e, m0, rows, nt;                                                                        \
+  for (int jt = blockIdx.x >> 3; row_tile_at<C::BM>(g, blockIdx.x & 7, jt, e, m0, rows, nt); \
+       jt += gridDim.x >> 3)
+
+#define TILE_SYNC()                                        \
+  if (jt != (int)(blockIdx.x >> 3)) __syncthreads();
+
+#define DMA_PROLOGUE(C)                                                              \
+  __shared__ __attribute__((aligned(1024))) uint16_t S0[C::STAGE];                  \
+  __shared__ __attribute__((aligned(1024))) uint16_t S1[C::STAGE];                  \
+  __shared__ __attribute__((aligned(1024))) uint16_t S2[C::STAGE];                  \
+  __shared__ __attribute__((aligned(1024))) uint16_t S3[C::STAGE];                  \
+  const int lane = threadIdx.x & 63;                                                \
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);                \
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+// ---------------------------------------------------------------- gate_up fwd
+// B rows: 32-row groups alternate gate and up rows of the same 32 activation
+// columns (see epi_gate_up).
+template <class C, bool WRITE_A, bool WRITE_Z>
+__global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
+  DMA_PROLOGUE(C)
+  TILE_LOOP(C) {
+    TILE_SYNC()
+    const int H = g.H, I = g.I;
+    const uint16_t* X = (const uint16_t*)g.A;
+    const int j0 = nt * (C::BN / 2);
+    const int* tok = g.tok_of_pos;
+    RowSrc<C::NBA> as;
+    RowSrc<C::NBB> bs;
+    // hidden rows of the expert's tokens (byte offsets from X); gate or up
+    // rows of the expert's weights (a 16-row load stays in one 32-row group)
+    as.init([&](int r, const char*& b, uint32_t& o) {
+      b = (const char*)X;
+      o = (uint32_t)((size_t)tok[m0 + min(r, rows - 1)] * H * 2);
+    }, wave, lane);
+    bs.init([&](int r, const char*& b, uint32_t& o) {
+      const int q = r >> 5;
+      const int j = min(j0 + ((q >> 1) << 5) + (r & 31), I - 1);
+      b = (const char*)gu_row((const uint16_t*)g.gu_g, (const uint16_t*)g.gu_u, g.gu_es, g.gu_rs, e, q & 1, 0);
+      o = (uint32_t)((size_t)g.gu_rs * j * 2);
+    }, wave, lane);
+    f32x16 acc[C::FM][C::FN];
+    dma_mainloop<C, false, false>(as, bs, H / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    epi_gate_up<C, uint16_t, WRITE_A, WRITE_Z>(g, acc, m0, rows, j0, wm, wn, lane);
+  }
+}
+
+// ---------------------------------------------------------------- down fwd
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
+  DMA_PROLOGUE(C)
+  TILE_LOOP(C) {
+    TILE_SYNC()
+    const int H = g.H, I = g.I;
+    const uint16_t* Aa = (const uint16_t*)g.A;
+    const uint16_t* W = (const uint16_t*)g.B + (size_t)e * H * I;
+    const int n0 = nt * C::BN;
+    RowSrc<C::NBA> as;
+    RowSrc<C::NBB> bs;
+    as.init([&](int r, const char*& b, uint32_t& o) {
+      b = (const char*)(Aa + (size_t)m0 * I);
+      o = (uint32_t)(min(r, rows - 1) * I * 2);
+    }, wave, lane);
+    bs.init([&](int r, const char*& b, uint32_t& o) {
+      b = (const char*)W;
+      o = (uint32_t)((size_t)min(n0 + r, H - 1) * I * 2);
+    }, wave, lane);
+    f32x16 acc[C::FM][C::FN];
+    dma_mainloop<C, false, false>(as, bs, I / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    epi_down<C>(g, acc, m0, rows, n0, wm, wn, lane);
+  }
+}
+
+// ---------------------------------------------------------------- down dgrad
+// r[p, i] = sum_h dYp[p, h] Wd[e][h, i]: the weights are k (= h) rows of I columns.
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
+  DMA_PROLOGUE(C)
+  TILE_LOOP(C) {
+    TILE_SYNC()
+    const int H = g.H, I = g.I;
+    const uint16_t* dYp = (const uint16_t*)g.A;
+    const uint16_t* W = (const uint16_t*)g.B + (size_t)e * H * I;
+    const int n0 = nt * C::BN;
+    RowSrc<C::NBA> as;
+    ColSrc<C::NBB> bs;
+    as.init([&](int r, const char*& b, uint32_t& o) {
+      b = (const char*)(dYp + (size_t)m0 * H);
+      o = (uint32_t)(min(r, rows - 1) * H * 2);
+    }, wave, lane);
+    bs.init(W, W, I, H, I, n0, wave, lane);
+    f32x16 acc[C::FM][C::FN];
+    dma_mainloop<C, false, true>(as, bs, H / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    __syncthreads();   // every wave done with the stages: S0 holds the row reduction
+    epi_down_dgrad<C, uint16_t>(g, acc, m0, rows, n0, nt, wm, wn, lane, (float*)S0);
+  }
+}
+
+// ---------------------------------------------------------------- gate_up dgrad
+// dXp[p, h] = sum over the 2I dZ columns m of dZ[p, m] (gate or up row of m)[h]:
+// the weights are k (= m) rows of H columns, in dZ-column order (the fused
+// layouts' row order; separate tensors switch to the up tensor at m = I).
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
+  DMA_PROLOGUE(C)
+  TILE_LOOP(C) {
+    TILE_SYNC()
+    const int H = g.H, I = g.I, I2 = 2 * g.I;
+    const uint16_t* dZ = (const uint16_t*)g.A;
+    const int n0 = nt * C::BN;
+    const uint16_t* bg = (const uint16_t*)g.gu_g + g.gu_es * e;
+    const uint16_t* bu = (const uint16_t*)g.gu_u + g.gu_es * e;
+    RowSrc<C::NBA> as;
+    ColSrc<C::NBB> bs;
+    as.init([&](int r, const char*& b, uint32_t& o) {
+      b = (const char*)(dZ + (size_t)m0 * I2);
+      o = (uint32_t)(min(r, rows - 1) * I2 * 2);
+    }, wave, lane);
+    if (g.gu_sep) bs.init(bg, bu, H, I, H, n0, wave, lane);
+    else bs.init(bg, bg, H, I2, H, n0, wave, lane);
+    f32x16 acc[C::FM][C::FN];
+    dma_mainloop<C, false, true>(as, bs, I2 / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    epi_gate_up_dgrad<C>(g, acc, m0, rows, n0, wm, wn, lane);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+// One workgroup per CU, a whole number per XCD (the tile loop walks the rest).
+static long persistent_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  return (cus / 8) * 8;
+}
+
+// bf16, k dimensions in whole steps of 32, and every byte offset the loads
+// form below 2^31: hidden rows from the start of hidden (T * H * 2), an
+// expert's weight rows from its gate or up base (2 * I * H * 2), a tile's
+// rows from its first row (256 * 2I * 2).
+bool dma_enabled(const GemmProblem& pb) {
+  const long lim = 1L << 31;
+  return pb.dtype == 0 && pb.H % 32 == 0 && pb.I % 32 == 0 && (long)pb.T * pb.H * 2 < lim &&
+         4L * pb.I * pb.H < lim && 256L * 4 * pb.I < lim && 256L * 2 * pb.H < lim;
+}
+
+// Experts of fewer slots keep the other engine's 128- or 192-row tiles: a
+// 256-row tile over a few hundred slots is mostly empty.
+constexpr int kLargeTileMinSlots = 512;
+int large_tile_min_slots(const GemmProblem& pb) { return dma_enabled(pb) ? kLargeTileMinSlots : 0x7fffffff; }
+
+hipError_t dma_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
+                       hipStream_t s) {
+  using C = DCfgB;
+  GemmProblem p = pb;
+  p.tile_set = 1;
+  GArgs g = base_args(p, C::BM);
+  g.A = X; g.B = Wgu; g.out0 = a_out; g.out1 = z_out;
+  set_gu(g, pb, Wgu, nullptr, 0);
+  g.ntn = (pb.I + C::BN / 2 - 1) / (C::BN / 2);
+  const long grid = persistent_grid();
+  const char* name = a_out ? "gate_up_glu_big" : "gate_up_z_big";
+  return run_kernel(name, s, [&] {
+    if (a_out && z_out) dma_gate_up_kernel<C, true, true><<<grid, C::NT, 0, s>>>(g);
+    else if (a_out) dma_gate_up_kernel<C, true, false><<<grid, C::NT, 0, s>>>(g);
+    else dma_gate_up_kernel<C, false, true><<<grid, C::NT, 0, s>>>(g);
+  });
+}
+
+hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
+  using C = DCfgB;
+  GemmProblem p = pb;
+  p.tile_set = 1;
+  GArgs g = base_args(p, C::BM);
+  g.A = a; g.B = Wd; g.out0 = Yp;
+  g.ntn = (pb.H + C::BN - 1) / C::BN;
+  const long grid = persistent_grid();
+  return run_kernel("down_weighted_big", s, [&] { dma_down_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+}
+
+hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
+                          float* partials, int nparts, hipStream_t s) {
+  using C = DCfgB;
+  GemmProblem p = pb;
+  p.tile_set = 1;
+  GArgs g = base_args(p, C::BM);
+  g.A = dY; g.B = Wd; g.Z = Z; g.out0 = dZ; g.out1 = aw; g.partials = partials;
+  g.ntn = (pb.I + C::BN - 1) / C::BN;
+  g.nparts = nparts;
+  const long grid = persistent_grid();
+  return run_kernel("down_dgrad_glu_bwd_big", s, [&] { dma_down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+}
+
+hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
+  using C = DCfgB;
+  GemmProblem p = pb;
+  p.tile_set = 1;
+  GArgs g = base_args(p, C::BM);
+  g.A = dZ; g.B = Wgu; g.out0 = dXp;
+  set_gu(g, pb, Wgu, nullptr, 0);
+  g.ntn = (pb.H + C::BN - 1) / C::BN;
+  const long grid = persistent_grid();
+  return run_kernel("gate_up_dgrad_big", s, [&] { dma_gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+}
+
+}  // namespace moe

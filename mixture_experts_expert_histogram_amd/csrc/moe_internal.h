@@ -10,16 +10,25 @@ namespace moe {
 constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_CHUNK = 512;
 constexpr int MAX_E = 1024;
-// M-tile heights for which the routing scan writes a tile prefix table.
-constexpr int N_TILE_BM = 5;              // 32, 64, 128, 256, 192
-__host__ __device__ constexpr int tile_bm(int j) { return j < 4 ? 32 << j : 192; }
+// Tile prefix tables the routing scan writes, one per (M-tile height, set of
+// experts): tables 0-4 cover every expert with 32, 64, 128, 256 and 192-row
+// tiles; table 5 covers the experts with at least big_min slots in 256-row
+// tiles (the large-tile engine), tables 6 and 7 the experts below it in 128
+// and 192-row tiles.
+constexpr int N_TILE_TABLES = 8;
+constexpr int TILE_BIG256 = 5, TILE_SMALL128 = 6, TILE_SMALL192 = 7;
+__host__ __device__ constexpr int tile_bm(int j) {
+  return j < 4 ? 32 << j : j == 4 ? 192 : j == TILE_BIG256 ? 256 : j == TILE_SMALL128 ? 128 : 192;
+}
+// 0: every expert, 1: experts with at least big_min slots, 2: the others
+__host__ __device__ constexpr int tile_set(int j) { return j < 5 ? 0 : j == TILE_BIG256 ? 1 : 2; }
 
 // Device views of the routing state that lives in the workspace.
 struct RouteState {
   int32_t* status;        // [4]  status[0] = number of slots with a bad id
   int32_t* counts;        // [E]
   int32_t* offsets;       // [E+1]
-  int32_t* tile_prefix;   // [N_TILE_BM][E+1]
+  int32_t* tile_prefix;   // [N_TILE_TABLES][E+1]
   int32_t* expert_order;  // [E] experts by descending count (ties: lower id)
   int32_t* blk_hist;      // [nblk][E] (histogram, then per-block base)
   int32_t* blk_bad;       // [nblk]
@@ -28,6 +37,7 @@ struct RouteState {
   int32_t* tok_of_pos;    // [S] token of the slot at each position
   float* w_of_pos;        // [S] routing weight of the slot at each position
   int nblk;
+  int big_min;            // experts with at least this many slots use the large-tile engine
 };
 
 // Host side: optional timing events around each kernel launch (api.cpp).
@@ -74,6 +84,9 @@ struct GemmProblem {
   // (layout is then the concatenated one for Z and dZ); null when fused
   const void* w_up = nullptr;
   void* dw_up = nullptr;
+  // experts a token-row launch covers: 0 all, 1 those with at least
+  // rs->big_min slots (large-tile engine), 2 the others
+  int tile_set = 0;
 };
 // Per-slot buffers are indexed by the expert-sorted position p.
 // forward gate_up projection + GLU: writes a [S,I] (dtype, if a_out) and Z fp32 [S,2I] (if z_out)
@@ -94,6 +107,11 @@ hipError_t launch_wgrad_down(const GemmProblem& pb, const void* dY, const void* 
                              hipStream_t stream);
 hipError_t launch_wgrad_gate_up(const GemmProblem& pb, const void* dZ, const void* X, void* dWgu,
                                 hipStream_t stream);
+
+// Experts with at least this many slots take the large-tile engine in every
+// token-row GEMM of the problem (INT_MAX: none); set in the routing state
+// before routing.
+int large_tile_min_slots(const GemmProblem& pb);
 
 // rows dst[p] = src[tok_of_pos[p]] of width `row_bytes` (a multiple of 16)
 hipError_t launch_gather_rows(const void* src, const int32_t* tok_of_pos, int S, size_t row_bytes, void* dst,
