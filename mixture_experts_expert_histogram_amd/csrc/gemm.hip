@@ -1706,6 +1706,7 @@ static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const voi
     const hipError_t e2 = pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax, kLongMin)
                                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax, kLongMin);
     if (e2 != hipSuccess) return e2;
+    if (dma_wgrad_enabled(pb)) return dma_wgrad(pb, GU, A, B, dW, kLongMin, s);
     return pb.gdtype == 0 ? wgrad_long_impl<GU, uint16_t>(pb, A, B, dW, s)
                           : wgrad_long_impl<GU, float>(pb, A, B, dW, s);
   }

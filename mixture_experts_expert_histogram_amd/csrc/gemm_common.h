@@ -383,6 +383,10 @@ hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* 
 hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
                           float* partials, int nparts, hipStream_t s);
 hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s);
+// weight gradients (dW[e] = A_e^T B_e) of the experts with more than hot_min positions
+bool dma_wgrad_enabled(const GemmProblem& pb);
+hipError_t dma_wgrad(const GemmProblem& pb, bool gate_up, const void* A, const void* B, void* dW, int hot_min,
+                     hipStream_t s);
 
 // Tile table of a kernel with bm-row tiles over the problem's set of experts.
 inline int tile_table(const GemmProblem& pb, int bm) {

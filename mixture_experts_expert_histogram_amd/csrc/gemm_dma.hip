@@ -130,19 +130,27 @@ struct RowSrc {
 // are rows of base0, the others rows k - ksplit of base1 (ksplit a multiple
 // of 32, so a step takes one side); ld elements per row; columns past the
 // valid ones are clamped.
-template <int NB>
+//
+// CLAMP (the weight gradients, whose k is an expert's positions): k rows
+// past kmax read row kmax instead, so the ragged last step stays inside the
+// expert's rows; the kernel zeroes what those rows put into LDS where it
+// matters (dma_zero_rows).
+template <int NB, bool CLAMP = false>
 struct ColSrc {
   const char* b0;
   const char* b1;
-  uint32_t off[NB];   // bytes from a step's first k row to this lane's 16 bytes
+  uint32_t off[NB];   // bytes from a step's first k row to this lane's 16 bytes (no CLAMP)
+  uint32_t coff[NB];  // bytes of this lane's 16 bytes within a k row (CLAMP)
+  int kr[NB];         // this lane's k row within a step (CLAMP)
   uint32_t row_bytes;
-  int ksplit;
+  int ksplit, kmax;
   __device__ __forceinline__ void init(const uint16_t* base0, const uint16_t* base1, long ld, int ksplit_,
-                                       int ncols, int c0, int wave, int lane) {
+                                       int ncols, int c0, int wave, int lane, int kmax_ = 0x7fffffff) {
     b0 = uniform_ptr(base0);
     b1 = uniform_ptr(base1);
     row_bytes = (uint32_t)(ld * 2);
     ksplit = ksplit_;
+    kmax = kmax_;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int b = wave * NB + j;
@@ -150,17 +158,37 @@ struct ColSrc {
       const int chunk = (lane & 15) ^ ((krow & 3) << 2);
       const int col = min(c0 + (b >> 3) * 128 + chunk * 8, ncols - 8);
       off[j] = krow * row_bytes + col * 2;
+      coff[j] = col * 2;
+      kr[j] = krow;
     }
   }
   __device__ __forceinline__ void issue(int kt, uint16_t* tile, int wave) const {
     const int k0 = kt * 32;
-    const bool lo = k0 < ksplit;
-    const char* b = lo ? b0 : b1;
-    const uint32_t koff = (uint32_t)(lo ? k0 : k0 - ksplit) * row_bytes;
+    if constexpr (CLAMP) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) lds_dma16(b, koff + off[j], tile + (wave * NB + j) * 512);
+      for (int j = 0; j < NB; ++j)
+        lds_dma16(b0, (uint32_t)min(k0 + kr[j], kmax) * row_bytes + coff[j], tile + (wave * NB + j) * 512);
+    } else {
+      const bool lo = k0 < ksplit;
+      const char* b = lo ? b0 : b1;
+      const uint32_t koff = (uint32_t)(lo ? k0 : k0 - ksplit) * row_bytes;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) lds_dma16(b, koff + off[j], tile + (wave * NB + j) * 512);
+    }
   }
 };
+
+// Zero the k rows from kvalid on that this wave's NB loads of a [32][COLS]
+// column-half tile wrote (each lane its own 16 bytes), so rows past an
+// expert's last position add nothing.  The wave's own loads must have landed.
+template <int NB>
+__device__ __forceinline__ void dma_zero_rows(uint16_t* tile, int kvalid, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int b = wave * NB + j;
+    if ((b & 7) * 4 + (lane >> 4) >= kvalid) *(uint4*)(tile + b * 512 + lane * 8) = make_uint4(0, 0, 0, 0);
+  }
+}
 
 // 32 columns x 16 k of a [32][128]-half tile (columns from cb), in the
 // fragment layout of the k-contiguous reads: lane -> column cb + lane % 32,
@@ -222,11 +250,20 @@ __device__ __forceinline__ void dma_issue(const AS& as, const BS& bs, int kt, ui
 }
 
 // Step kt on stage Sc; Sp (read by step kt-1) is refilled with step kt+3.
-template <class C, bool A_MN, bool B_MN, class AS, class BS>
-__device__ __forceinline__ void dma_step(const AS& as, const BS& bs, int kt, int last, const uint16_t* Sc,
+// ZERO: in the last step, k rows from klast on of the A tile (column halves)
+// are zeroed before the barrier (a ragged k dimension).
+template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
+__device__ __forceinline__ void dma_step(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc,
                                          uint16_t* Sp, f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn,
-                                         int lane) {
+                                         int lane, int klast = 32) {
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));   // own loads of step kt landed
+  if constexpr (ZERO) {
+    if (kt == last && klast < 32) {
+      asm volatile("" ::: "memory");   // the zeros follow the wait for the loads they overwrite
+      dma_zero_rows<C::NBA>(Sc, klast, wave, lane);
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));
+    }
+  }
   __builtin_amdgcn_s_barrier();                                          // everyone's; Sp read by all
   dma_issue<C>(as, bs, min(kt + C::NSTAGE - 1, last), Sp, wave);
   DFrags<C> f0, f1;
@@ -238,10 +275,10 @@ __device__ __forceinline__ void dma_step(const AS& as, const BS& bs, int kt, int
 
 // acc = A . B^T over nk steps of 32 k.  S0..S3 are the kernel's four stage
 // arrays (A tile, then B tile).  Ends with every load landed.
-template <class C, bool A_MN, bool B_MN, class AS, class BS>
+template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
 __device__ __forceinline__ void dma_mainloop(const AS& as, const BS& bs, int nk, uint16_t* S0, uint16_t* S1,
                                              uint16_t* S2, uint16_t* S3, f32x16 (&acc)[C::FM][C::FN], int wave,
-                                             int wm, int wn, int lane) {
+                                             int wm, int wn, int lane, int klast = 32) {
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -254,14 +291,14 @@ __device__ __forceinline__ void dma_mainloop(const AS& as, const BS& bs, int nk,
   dma_issue<C>(as, bs, min(2, last), S2, wave);
   int kt = 0;
   for (; kt + 4 <= nk; kt += 4) {
-    dma_step<C, A_MN, B_MN>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane);
-    dma_step<C, A_MN, B_MN>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane);
-    dma_step<C, A_MN, B_MN>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane);
-    dma_step<C, A_MN, B_MN>(as, bs, kt + 3, last, S3, S2, acc, wave, wm, wn, lane);
+    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane, klast);
+    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane, klast);
+    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane, klast);
+    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 3, last, S3, S2, acc, wave, wm, wn, lane, klast);
   }
-  if (kt < nk) dma_step<C, A_MN, B_MN>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane);
-  if (kt + 1 < nk) dma_step<C, A_MN, B_MN>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane);
-  if (kt + 2 < nk) dma_step<C, A_MN, B_MN>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane);
+  if (kt < nk) dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane, klast);
+  if (kt + 1 < nk) dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane, klast);
+  if (kt + 2 < nk) dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane, klast);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no load may outlive the tile (or the workgroup's LDS)
 }
 
@@ -397,6 +434,84 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- weight gradients
+// dW[e] = A_e^T B_e over the expert's positions (k), for experts with more
+// than hot_min positions: GATE_UP, A = dZ [S, 2I] and B = Xp [S, H]; else
+// A = dYp [S, H] and B = aw [S, I].  Both operands are position-major, so
+// both tiles are [32 k][256] column halves.  The expert's k count is ragged:
+// the last step's k rows past it read the expert's last position and are
+// zeroed in A's tile.  A persistent grid deals chunks of 32 tiles (an XCD's
+// 32 workgroups) round-robin to the XCDs, so every XCD gets a share of every
+// expert (one hot expert can hold a fifth of all positions); inside an
+// expert, groups of 8 M-tiles run N-tile by N-tile, so a chunk's tiles share
+// 4 B column blocks and 8 A column blocks in one L2.
+template <class C, bool GATE_UP, typename OutT>
+__global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
+  DMA_PROLOGUE(C)
+  const int I = g.I, H = g.H;
+  const int M = GATE_UP ? 2 * I : H, N = GATE_UP ? H : I;
+  {   // no expert above hot_min (the host cannot tell without a sync): leave at once
+    const int e0 = g.expert_order[0];
+    if (g.offsets[e0 + 1] - g.offsets[e0] <= g.hot_min) return;
+  }
+  int l = 0, h = g.E;   // l = leading experts (by count, descending) above hot_min
+  while (l < h) {
+    const int mid = (l + h) >> 1;
+    const int e = g.expert_order[mid];
+    if (g.offsets[e + 1] - g.offsets[e] > g.hot_min) l = mid + 1; else h = mid;
+  }
+  const int ntm = g.ntm, ntn = g.ntn, per_e = ntm * ntn;
+  const int total = l * per_e;
+  const uint16_t* Ag = (const uint16_t*)g.A;
+  const uint16_t* Bg = (const uint16_t*)g.B;
+  OutT* dW = (OutT*)g.out0;
+  // this XCD's j-th tile, increasing in j: the first one past the end ends the loop
+  for (int j = blockIdx.x >> 3;; j += gridDim.x >> 3) {
+    const int t = dealt_tile<32>(j, total);
+    if (t < 0) break;
+    if (j != (int)(blockIdx.x >> 3)) __syncthreads();   // the previous tile's stage reads are done
+    const int er = t / per_e, local = t - er * per_e;
+    const int e = g.expert_order[er];
+    const int off = g.offsets[e], cnt = g.offsets[e + 1] - off;   // cnt > hot_min > 0
+    const int gsz = kRowTileGroup * ntn;
+    const int grp = local / gsz, rem = local - grp * gsz;
+    const int gm = min(kRowTileGroup, ntm - grp * kRowTileGroup);
+    const int nt = rem / gm, mt = grp * kRowTileGroup + (rem - nt * gm);
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    const uint16_t* Ae = Ag + (size_t)off * M;
+    const uint16_t* Be = Bg + (size_t)off * N;
+    ColSrc<C::NBA, true> as;
+    ColSrc<C::NBB, true> bs;
+    as.init(Ae, Ae, M, 0, M, m0, wave, lane, cnt - 1);
+    bs.init(Be, Be, N, 0, N, n0, wave, lane, cnt - 1);
+    const int nk = (cnt + 31) >> 5;
+    f32x16 acc[C::FM][C::FN];
+    dma_mainloop<C, true, true, true>(as, bs, nk, S0, S1, S2, S3, acc, wave, wm, wn, lane, cnt - (nk - 1) * 32);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
+      if (m >= M) continue;
+      OutT* row;
+      if (GATE_UP && g.gu_sep) {   // separate dW_gate, dW_up: row m is a dZ column
+        int up, jj;
+        zcol(m, I, g.layout, up, jj);
+        row = gu_row((OutT*)g.dgu_g, (OutT*)g.dgu_u, g.gu_es, g.gu_rs, e, up, jj);
+      } else {
+        row = dW + ((size_t)e * M + m) * N;
+      }
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
+          if (n < N)
+            store4<OutT>(row + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
+                         acc[fm][fn][vg * 4 + 3]);
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 // One workgroup per CU, a whole number per XCD (the tile loop walks the rest).
 static long persistent_grid() {
@@ -474,6 +589,38 @@ hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* 
   g.ntn = (pb.H + C::BN - 1) / C::BN;
   const long grid = persistent_grid();
   return run_kernel("gate_up_dgrad_big", s, [&] { dma_gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+}
+
+// Weight gradients of the experts with more than hot_min positions; every
+// position row of either operand must sit below 2^31 bytes from the start.
+bool dma_wgrad_enabled(const GemmProblem& pb) {
+  const long lim = 1L << 31;
+  return dma_enabled(pb) && (long)pb.S * 4 * pb.I < lim && (long)pb.S * 2 * pb.H < lim;
+}
+
+template <bool GU, typename OutT>
+static hipError_t dma_wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, int hot_min,
+                                 hipStream_t s) {
+  using C = DCfgB;
+  const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
+  GArgs g = base_args(pb, C::BM);
+  g.A = A; g.B = B; g.out0 = dW;
+  if (GU) set_gu(g, pb, nullptr, dW, sizeof(OutT));
+  g.ntm = (M + C::BM - 1) / C::BM;
+  g.ntn = (N + C::BN - 1) / C::BN;
+  g.hot_min = hot_min;
+  const long grid = persistent_grid();
+  return run_kernel(GU ? "wgrad_gate_up_long" : "wgrad_down_long", s,
+                    [&] { dma_wgrad_kernel<C, GU, OutT><<<grid, C::NT, 0, s>>>(g); });
+}
+
+hipError_t dma_wgrad(const GemmProblem& pb, bool gate_up, const void* A, const void* B, void* dW, int hot_min,
+                     hipStream_t s) {
+  if (gate_up)
+    return pb.gdtype == 0 ? dma_wgrad_impl<true, uint16_t>(pb, A, B, dW, hot_min, s)
+                          : dma_wgrad_impl<true, float>(pb, A, B, dW, hot_min, s);
+  return pb.gdtype == 0 ? dma_wgrad_impl<false, uint16_t>(pb, A, B, dW, hot_min, s)
+                        : dma_wgrad_impl<false, float>(pb, A, B, dW, hot_min, s);
 }
 
 }  // namespace moe

@@ -8,6 +8,10 @@ the same call.  H = 288 and I = 160 leave ragged N-tiles in every product
 hidden columns; the input gradients: 160 and 32 of 256).  Z is saved or
 recomputed (the Z-only gate_up kernel); gate and up weights are fused in
 either layout or separate tensors.
+
+The weight gradients of experts above 512 slots take the large-tile kernel
+too: k (the expert's slots) is ragged, so its last 32-slot step reads the
+expert's last slot again and zeroes those rows of the dZ / dY tile.
 """
 import numpy as np
 import pytest
@@ -53,3 +57,32 @@ def test_large_tile_two_slots_per_token():
     ids = flat.reshape(T, K).astype(np.int32)
     inp = small_inputs(T, H, I, E, K, "bf16", "clamped", "interleaved", seed=57, ids=ids)
     run_and_compare(inp, save=True, grad_dtype="bf16")
+
+
+# remainders of the 32-slot step: 2080 -> 0, 1055 -> 31, 777 -> 9, 544 -> 0,
+# 513 -> 1, 600 -> 24; 40 and 0 stay on the other kernels
+WG_COUNTS = [2080, 1055, 777, 544, 513, 600, 40, 0]
+
+
+def weight_grad_inputs(layout, seed, H=544, I=1056):
+    E, K = len(WG_COUNTS), 1
+    T = sum(WG_COUNTS)
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(np.repeat(np.arange(E), WG_COUNTS)).reshape(T, K).astype(np.int32)
+    return small_inputs(T, H, I, E, K, "bf16", "swiglu", layout, seed=seed, ids=ids)
+
+
+@pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
+def test_large_tile_weight_grads(grad_dtype):
+    """dW_gate_up [2I = 2112, H = 544]: 9 M-tiles of 256 (two groups of 8,
+    the last 64 rows wide) by 3 N-tiles (the last 32 wide); dW_down
+    [H = 544, I = 1056]: 3 by 5 (the last 32 wide)."""
+    run_and_compare(weight_grad_inputs("interleaved", 61), save=True, grad_dtype=grad_dtype, poison=True)
+
+
+@pytest.mark.parametrize("layout", ["interleaved", "concat"])
+def test_large_tile_weight_grads_separate(layout):
+    """Separate gate and up gradient tensors: a 256-row tile of dZ columns
+    maps to rows of both tensors (interleaved) or straddles the boundary
+    between them at I = 1056 (concatenated)."""
+    check_separate(weight_grad_inputs(layout, 63), "swiglu", layout, "bf16", "bf16", True)
