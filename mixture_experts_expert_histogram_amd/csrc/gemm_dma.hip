@@ -1,37 +1,41 @@
-// Large-tile engine for the token-row GEMMs of experts with many slots.
+// Large-tile engine for the token-row GEMMs and weight gradients of experts
+// with many slots.
 //
-// When an expert holds hundreds to tens of thousands of slots its gate_up,
-// down and input-gradient products are dense GEMMs bound by the matrix
-// cores, not by the weight stream.  For those experts this engine computes
-// 256 x 256 tiles on 8 waves (2 x 4, 128 x 64 per wave) of
-// v_mfma_f32_32x32x16_bf16, with both operands moved from global memory
-// straight into LDS by global_load_lds_dwordx4 (no staging registers, no
-// ds_write), through a ring of four LDS stages of BK = 32:
+// When an expert holds hundreds to tens of thousands of slots its products
+// are dense GEMMs bound by the matrix cores, not by the weight stream.  For
+// those experts this engine computes 256 x 256 tiles on 8 waves (2 x 4,
+// 128 x 64 per wave) of v_mfma_f32_32x32x16_bf16, with both operands moved
+// from global memory straight into LDS by global_load_lds_dwordx4 (no staging
+// registers, no ds_write), through a ring of five LDS stages of BK = 32 (all
+// 160 KB of LDS):
 //
+// * Ping-pong: the two row halves of waves (one wave of each per SIMD) run
+//   half a step apart, so on every SIMD one wave issues MFMAs while the other
+//   refills a stage and reads its fragments (pp_step).
 // * Every step starts with a wait for the wave's own loads of that step
-//   (vmcnt, three steps of loads stay in flight) and a barrier, then refills
-//   the stage the previous step read with the step three ahead, then reads
-//   the fragments of the current stage and runs its MFMAs.
-// * The four stages are four distinct __shared__ arrays, the ring is unrolled
-//   by four and every refill is issued unconditionally (clamped to the last
-//   step), so the compiler's wait insertion can tell the stage being read from
-//   the stages in flight and never drains the ring (one array, or a branch
-//   around a refill, made it wait for every load before each read).
-// * The barrier is a plain s_barrier after an explicit wait (vmcnt(8),
-//   lgkmcnt(0)); __syncthreads() would also wait for every load in flight.
+//   (vmcnt; three steps of loads stay in flight) and a plain s_barrier;
+//   __syncthreads() would also wait for every load in flight.
+// * The five stages are five distinct __shared__ arrays, the ring is unrolled
+//   by five and every refill is issued unconditionally (clamped to the last
+//   step), so the wait counts are constants.
 // * A load writes 64 lanes x 16 bytes to consecutive LDS bytes; the tiles'
 //   XOR swizzles come from permuting which 16 bytes of global memory each
-//   lane reads.
+//   lane reads (no LDS bank conflicts, measured).
 //
-// Measured on a dense 24576 x 5632 x 2880 bf16 product: 981 TFLOP/s, against
-// 936 with register-staged loads and ds_write (the LDS writes of the staged
-// tiles were the largest cost: 1195 TFLOP/s with them left out) and 1006 for
-// hipBLASLt on the same shape.
+// Measured limits (rocprofv3 counters on the Zipf batch): the token-row
+// kernels keep the texture data path that feeds LDS 86-94 % busy at about
+// half the MFMA rate; with 64-byte row segments per load (k-contiguous
+// operands, BK = 32) it moves about 17 bytes per clock and CU.  Probes with
+// 128-byte segments (BK = 64, two stages, 4 waves of 128 x 128) move 28 but
+// stall elsewhere and land at the same throughput; hipBLASLt reaches about
+// 1.35 PFLOP/s on a plain 24576 x 5632 x 2880 product against about 1.0 here.
 //
 // Operands contiguous along k are [row][32] tiles (64-byte rows, 16-byte
 // chunks XORed with (row / 4) % 4); operands contiguous along m or n (the
-// weights of the input gradients) are [32][128] column halves read with
-// ds_read_b64_tr_b16, like the other engine's.  K must be a multiple of 32.
+// weights of the input gradients, both operands of the weight gradients) are
+// [32][128] column halves read with ds_read_b64_tr_b16, like the other
+// engine's.  K must be a multiple of 32 (the weight gradients' ragged k is
+// handled by clamped rows and zeroed LDS rows).
 #include "gemm_common.h"
 
 namespace moe {
@@ -72,10 +76,10 @@ __device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint16
       : "memory", "m0");
 }
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NSTAGE_ = 4>
 struct DCfg {
   using elem = uint16_t;
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32, NSTAGE = 4;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32, NSTAGE = NSTAGE_;
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK, STAGE = A_ELEMS + B_ELEMS;
@@ -84,7 +88,7 @@ struct DCfg {
   static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "whole 1 KB loads per wave");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "column halves of 128");
 };
-using DCfgB = DCfg<256, 256, 2, 4>;
+using DCfgB = DCfg<256, 256, 2, 4, 5>;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt <= n and lgkmcnt = 0.
@@ -249,57 +253,88 @@ __device__ __forceinline__ void dma_issue(const AS& as, const BS& bs, int kt, ui
   bs.issue(kt, St + C::A_ELEMS, wave);
 }
 
-// Step kt on stage Sc; Sp (read by step kt-1) is refilled with step kt+3.
-// ZERO: in the last step, k rows from klast on of the A tile (column halves)
-// are zeroed before the barrier (a ragged k dimension).
-template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
-__device__ __forceinline__ void dma_step(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc,
-                                         uint16_t* Sp, f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn,
-                                         int lane, int klast = 32) {
+// Ping-pong schedule of the ring: the two row halves of waves (wm = 0, 1;
+// one wave of each on every SIMD) run half a step apart, so that on every
+// SIMD one wave issues MFMAs while the other reads fragments and issues
+// loads.  Every wave runs the same step (barrier, refill + reads, barrier,
+// MFMAs); the upper half passes one extra barrier first and the lower half
+// one at the end, so with barriers A_t, B_t of step t:
+//
+//   after A_t:  wm = 0 refills and reads step t | wm = 1 MFMAs of step t-1
+//   after B_t:  wm = 0 MFMAs of step t          | wm = 1 refills and reads step t
+//
+// Before A_t every wave's own loads of step t have landed (the lower half
+// waits before A_t, the upper one after its reads of step t-1) and, with a
+// ragged k, its rows of A past klast are zeroed.  The stage refilled with
+// step t+3 was read in step t-1 by both halves, before A_t (the upper half
+// waits for its reads with the same wait).  Two steps of loads stay in
+// flight at each wait.
+template <class C, bool ZERO>
+__device__ __forceinline__ void pp_land(int kt, int last, uint16_t* St, int wave, int lane, int klast) {
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));   // own loads of step kt landed
   if constexpr (ZERO) {
     if (kt == last && klast < 32) {
       asm volatile("" ::: "memory");   // the zeros follow the wait for the loads they overwrite
-      dma_zero_rows<C::NBA>(Sc, klast, wave, lane);
+      dma_zero_rows<C::NBA>(St, klast, wave, lane);
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));
     }
   }
-  __builtin_amdgcn_s_barrier();                                          // everyone's; Sp read by all
+}
+
+// Step kt on stage Sc; Sp (read in step kt-1) is refilled with step kt+3; Sn
+// holds step kt+1.
+template <class C, bool A_MN, bool B_MN, bool ZERO, class AS, class BS>
+__device__ __forceinline__ void pp_step(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc, uint16_t* Sp,
+                                        uint16_t* Sn, f32x16 (&acc)[C::FM][C::FN], bool hi, int wave, int wm, int wn,
+                                        int lane, int klast) {
+  if (!hi) pp_land<C, ZERO>(kt, last, Sc, wave, lane, klast);
+  __builtin_amdgcn_s_barrier();   // lower half: A_kt; upper half: B_kt
   dma_issue<C>(as, bs, min(kt + C::NSTAGE - 1, last), Sp, wave);
   DFrags<C> f0, f1;
   dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 0, f0, wm, wn, lane);
   dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 1, f1, wm, wn, lane);
+  if (hi) pp_land<C, ZERO>(kt + 1, last, Sn, wave, lane, klast);
+  __builtin_amdgcn_sched_barrier(0);   // no MFMA moves above the barrier
+  __builtin_amdgcn_s_barrier();   // lower half: B_kt; upper half: A_kt+1
+  __builtin_amdgcn_sched_barrier(0);
   dma_mma<C>(f0, acc);
   dma_mma<C>(f1, acc);
 }
 
-// acc = A . B^T over nk steps of 32 k.  S0..S3 are the kernel's four stage
-// arrays (A tile, then B tile).  Ends with every load landed.
 template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
-__device__ __forceinline__ void dma_mainloop(const AS& as, const BS& bs, int nk, uint16_t* S0, uint16_t* S1,
-                                             uint16_t* S2, uint16_t* S3, f32x16 (&acc)[C::FM][C::FN], int wave,
-                                             int wm, int wn, int lane, int klast = 32) {
+__device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, uint16_t* const (&St)[5],
+                                            f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn, int lane,
+                                            int klast = 32) {
+  static_assert(C::WM == 2, "two row halves of waves");
+  constexpr int NS = C::NSTAGE;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const bool hi = wm == 1;
   const int last = nk - 1;
-  dma_issue<C>(as, bs, 0, S0, wave);
-  dma_issue<C>(as, bs, min(1, last), S1, wave);
-  dma_issue<C>(as, bs, min(2, last), S2, wave);
-  int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane, klast);
-    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane, klast);
-    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane, klast);
-    dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 3, last, S3, S2, acc, wave, wm, wn, lane, klast);
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) dma_issue<C>(as, bs, min(u, last), St[u], wave);
+  if (hi) {   // A_0
+    pp_land<C, ZERO>(0, last, St[0], wave, lane, klast);
+    __builtin_amdgcn_s_barrier();
   }
-  if (kt < nk) dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt, last, S0, S3, acc, wave, wm, wn, lane, klast);
-  if (kt + 1 < nk) dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 1, last, S1, S0, acc, wave, wm, wn, lane, klast);
-  if (kt + 2 < nk) dma_step<C, A_MN, B_MN, ZERO>(as, bs, kt + 2, last, S2, S1, acc, wave, wm, wn, lane, klast);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no load may outlive the tile (or the workgroup's LDS)
+  int kt = 0;
+  for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      pp_step<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
+                                   wave, wm, wn, lane, klast);
+  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (kt + u < nk)
+      pp_step<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
+                                   wave, wm, wn, lane, klast);
+  if (!hi) __builtin_amdgcn_s_barrier();   // the upper half's A_nk
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 }
 
 // Persistent workgroups, one per CU: workgroup b walks tiles b / 8,
@@ -315,10 +350,13 @@ __device__ __forceinline__ void dma_mainloop(const AS& as, const BS& bs, int nk,
   if (jt != (int)(blockIdx.x >> 3)) __syncthreads();
 
 #define DMA_PROLOGUE(C)                                                              \
+  static_assert(C::NSTAGE == 4 || C::NSTAGE == 5, "ring of 4 or 5 stages");         \
   __shared__ __attribute__((aligned(1024))) uint16_t S0[C::STAGE];                  \
   __shared__ __attribute__((aligned(1024))) uint16_t S1[C::STAGE];                  \
   __shared__ __attribute__((aligned(1024))) uint16_t S2[C::STAGE];                  \
   __shared__ __attribute__((aligned(1024))) uint16_t S3[C::STAGE];                  \
+  __shared__ __attribute__((aligned(1024))) uint16_t S4[C::NSTAGE > 4 ? C::STAGE : 1]; \
+  uint16_t* const St[5] = {S0, S1, S2, S3, S4};                                     \
   const int lane = threadIdx.x & 63;                                                \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);                \
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -350,7 +388,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
       o = (uint32_t)((size_t)g.gu_rs * j * 2);
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    dma_mainloop<C, false, false>(as, bs, H / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, false>(as, bs, H / 32, St, acc, wave, wm, wn, lane);
     epi_gate_up<C, uint16_t, WRITE_A, WRITE_Z>(g, acc, m0, rows, j0, wm, wn, lane);
   }
 }
@@ -376,12 +414,125 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
       o = (uint32_t)((size_t)min(n0 + r, H - 1) * I * 2);
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    dma_mainloop<C, false, false>(as, bs, I / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, false>(as, bs, I / 32, St, acc, wave, wm, wn, lane);
     epi_down<C>(g, acc, m0, rows, n0, wm, wn, lane);
   }
 }
 
 // ---------------------------------------------------------------- down dgrad
+// The epilogue goes through LDS, so that its Z reads and dZ / aw stores move
+// whole rows.  The tile's r values go to the four stages in two halves of 128
+// rows (the waves of row half h write theirs: fragment fm into stage fm, 32
+// rows x 256 fp32 columns, 16-byte chunks XORed with row % 16), then each wave
+// takes rows 8q + wave of the half, lane l columns 4l .. 4l + 3: one
+// contiguous 2 KB (Z), 1 KB (dZ) and 512 B (aw) access per row and wave, in
+// batches of 2 rows with the next batch's Z loads in flight.  Written from
+// the accumulators, every lane of a wave hit 32 rows.
+__device__ __forceinline__ int epi_chunk(int row, int chunk) { return (row << 8) + ((chunk ^ (row & 15)) << 2); }
+
+template <class C>
+__device__ __forceinline__ void epi_r_to_lds(f32x16 (&acc)[C::FM][C::FN], float* const (&st)[4], int wn, int lane) {
+  static_assert(C::FM == 4 && C::BN == 256, "fragment fm of a 128-row half fills stage fm");
+  const int row = lane & 31;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int chunk = (wn * C::WTN + fn * 32 + acc_col4(vg, lane)) >> 2;
+        *(float4*)(st[fm] + epi_chunk(row, chunk)) =
+            make_float4(acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
+      }
+}
+
+// Z of one row at columns ic .. ic + 3 (interleaved: g, u pairs over 8 floats;
+// concatenated: gate, then up at + I).
+__device__ __forceinline__ void epi_z_load(const float* zr, int ic, int I, int layout, float4& z0, float4& z1) {
+  z0 = *(const float4*)(zr + (layout ? 2 * ic : ic));
+  z1 = *(const float4*)(zr + (layout ? 2 * ic + 4 : I + ic));
+}
+
+template <class C, int RB>
+__device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)[C::FM][C::FN], int m0, int rows,
+                                                   int n0, int nt, int wave, int wm, int wn, int lane,
+                                                   float* const (&st)[4]) {
+  static_assert(C::NW == 8 && C::WM == 2, "8 waves over rows 8q + wave of a 128-row half");
+  const int I = g.I, layout = g.layout;
+  const float* Z = (const float*)g.Z;
+  uint16_t* dZ = (uint16_t*)g.out0;
+  uint16_t* aw = (uint16_t*)g.out1;
+  const int i = n0 + lane * 4;
+  const bool col_ok = i < I;
+  const int ic = col_ok ? i : I - 4;   // I is a multiple of 4
+  const int slot = nt * 2 + (lane >> 5);   // 128-column partial slot of this lane's columns
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) epi_r_to_lds<C>(acc, st, wn, lane);
+    __syncthreads();
+    const int hrows = rows - h * 128;   // valid rows of this half (may be <= 0)
+    if (hrows > 0) {
+      float4 za[2][RB], zb[2][RB];
+      auto pos = [&](int q) { return m0 + h * 128 + min(q * 8 + wave, hrows - 1); };
+      auto load = [&](int b, int buf) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+          epi_z_load(Z + (size_t)pos(b * RB + r) * 2 * I, ic, I, layout, za[buf][r], zb[buf][r]);
+      };
+      auto process = [&](int b, int buf) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int q = b * RB + r, hr = q * 8 + wave;
+          const size_t p = (size_t)pos(q);
+          const float w = g.w_of_pos[p];
+          const float4 rv = *(const float4*)(st[q >> 2] + epi_chunk(hr & 31, lane));
+          const float4 z0 = za[buf][r], z1 = zb[buf][r];
+          float gv[4], uv[4];
+          if (layout) {
+            gv[0] = z0.x; uv[0] = z0.y; gv[1] = z0.z; uv[1] = z0.w;
+            gv[2] = z1.x; uv[2] = z1.y; gv[3] = z1.z; uv[3] = z1.w;
+          } else {
+            gv[0] = z0.x; gv[1] = z0.y; gv[2] = z0.z; gv[3] = z0.w;
+            uv[0] = z1.x; uv[1] = z1.y; uv[2] = z1.z; uv[3] = z1.w;
+          }
+          const float rr[4] = {rv.x, rv.y, rv.z, rv.w};
+          float dg[4], du[4], a[4], rs = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            a[c] = glu_bwd(gv[c], uv[c], w * rr[c], g.act, g.limit, g.alpha, dg[c], du[c]);
+            rs += rr[c] * a[c];
+          }
+          if (!col_ok) rs = 0.f;   // columns past I hold clamped weight columns
+          // sum over the 32 lanes of each 128-column slot, in a fixed order
+#pragma unroll
+          for (int d = 16; d >= 1; d >>= 1) rs += __shfl_xor(rs, d);
+          if (hr < hrows) {
+            uint16_t* dzr = dZ + p * 2 * I;
+            if (col_ok) {
+              if (layout) {
+                store4x2<uint16_t>(dzr + 2 * i, dg, du);
+              } else {
+                store4<uint16_t>(dzr + i, dg[0], dg[1], dg[2], dg[3]);
+                store4<uint16_t>(dzr + I + i, du[0], du[1], du[2], du[3]);
+              }
+              store4<uint16_t>(aw + p * I + i, w * a[0], w * a[1], w * a[2], w * a[3]);
+            }
+            if ((lane & 31) == 0 && slot * 128 < I) g.partials[p * g.nparts + slot] = rs;
+          }
+        }
+      };
+      constexpr int NB = 16 / RB;
+      load(0, 0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b + 1 < NB) load(b + 1, (b + 1) & 1);
+        process(b, b & 1);
+      }
+    }
+    if (h == 0) __syncthreads();   // half 0 read before half 1 overwrites it
+  }
+}
+
 // r[p, i] = sum_h dYp[p, h] Wd[e][h, i]: the weights are k (= h) rows of I columns.
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
@@ -400,9 +551,10 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
     }, wave, lane);
     bs.init(W, W, I, H, I, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    dma_mainloop<C, false, true>(as, bs, H / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
-    __syncthreads();   // every wave done with the stages: S0 holds the row reduction
-    epi_down_dgrad<C, uint16_t>(g, acc, m0, rows, n0, nt, wm, wn, lane, (float*)S0);
+    pp_mainloop<C, false, true>(as, bs, H / 32, St, acc, wave, wm, wn, lane);
+    __syncthreads();   // every wave done with the stages: they hold the epilogue's r values
+    float* const st[4] = {(float*)S0, (float*)S1, (float*)S2, (float*)S3};
+    dma_epi_down_dgrad<C, 2>(g, acc, m0, rows, n0, nt, wave, wm, wn, lane, st);
   }
 }
 
@@ -429,7 +581,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
     if (g.gu_sep) bs.init(bg, bu, H, I, H, n0, wave, lane);
     else bs.init(bg, bg, H, I2, H, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    dma_mainloop<C, false, true>(as, bs, I2 / 32, S0, S1, S2, S3, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, true>(as, bs, I2 / 32, St, acc, wave, wm, wn, lane);
     epi_gate_up_dgrad<C>(g, acc, m0, rows, n0, wm, wn, lane);
   }
 }
@@ -486,7 +638,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
     bs.init(Be, Be, N, 0, N, n0, wave, lane, cnt - 1);
     const int nk = (cnt + 31) >> 5;
     f32x16 acc[C::FM][C::FN];
-    dma_mainloop<C, true, true, true>(as, bs, nk, S0, S1, S2, S3, acc, wave, wm, wn, lane, cnt - (nk - 1) * 32);
+    pp_mainloop<C, true, true, true>(as, bs, nk, St, acc, wave, wm, wn, lane, cnt - (nk - 1) * 32);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
