@@ -105,6 +105,15 @@ def measured_traffic(kernel, workload, grad_dtype):
 # ------------------------------------------------------------------ per-kernel model
 RES_KMAX = 240   # the resident-operand weight gradient's limit (positions per expert)
 LONG_MIN = 512  # experts with more positions take the long-K weight gradient
+LARGE_MIN = 512  # experts with at least this many slots take the 256-row token-row tiles
+
+
+def large_tiles(wl):
+    """Whether the library runs the 256 x 256-tile engine for this workload's
+    big experts (bf16 operands, H and I multiples of 32, offsets in range)."""
+    lim = 1 << 31
+    return (wl.dtype == "bf16" and wl.H % 32 == 0 and wl.I % 32 == 0 and wl.T * wl.H * 2 < lim
+            and 4 * wl.I * wl.H < lim and 256 * 4 * wl.I < lim and 256 * 2 * wl.H < lim)
 def kernel_model(wl, counts, grad_bytes):
     """Algorithmic bytes and routed flops of one launch of each kernel.
 
@@ -120,18 +129,31 @@ def kernel_model(wl, counts, grad_bytes):
     """
     S, T, H, I = wl.S, wl.T, wl.H, wl.I
     eb = 2 if wl.dtype == "bf16" else 4
-    touched = int((counts > 0).sum())
-    Wgu = touched * 2 * I * H * eb
-    Wd = touched * H * I * eb
     m = {
-        "gate_up_glu": (Wgu + T * H * eb, 4.0 * S * H * I),
-        "down_weighted": (Wd, 2.0 * S * H * I),
         "combine": (S * H * 4 + T * H * eb + S * 4, 0.0),
         "gather_rows": (2 * S * H * eb + S * 4, 0.0),
-        "down_dgrad_glu_bwd": (Wd + T * H * eb, 2.0 * S * H * I),
-        "gate_up_dgrad": (Wgu, 4.0 * S * H * I),
         "topkw_reduce": (S * 4 * 2, 0.0),
     }
+
+    # Token-row products.  Experts with at least LARGE_MIN slots run on the
+    # 256-row tiles (*_big) when the workload allows them, the rest on the
+    # 128/192-row tiles; each part is charged its experts' weights and the
+    # hidden / output-gradient rows prorated by its slots.
+    def rows(sel, suffix):
+        touched = int(((counts > 0) & sel).sum())
+        s_part = int(counts[sel].sum())
+        tok = s_part / S if S else 0.0
+        Wgu, Wd = touched * 2 * I * H * eb, touched * H * I * eb
+        m["gate_up_glu" + suffix] = (Wgu + tok * T * H * eb, 4.0 * s_part * H * I)
+        m["down_weighted" + suffix] = (Wd, 2.0 * s_part * H * I)
+        m["down_dgrad_glu_bwd" + suffix] = (Wd + tok * T * H * eb, 2.0 * s_part * H * I)
+        m["gate_up_dgrad" + suffix] = (Wgu, 4.0 * s_part * H * I)
+    import numpy as np
+    counts = np.asarray(counts)
+    big = (counts >= LARGE_MIN) if large_tiles(wl) else np.zeros(len(counts), dtype=bool)
+    rows(~big, "")
+    if big.any():
+        rows(big, "_big")
     # Weight gradients.  With bf16 operands, experts with at most RES_KMAX
     # positions (and those without any) take the resident-operand kernel,
     # named wgrad_down / wgrad_gate_up, those with more than LONG_MIN the

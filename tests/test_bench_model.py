@@ -52,11 +52,14 @@ def test_projection_bytes_are_weights_and_layer_inputs():
     counts[:3] = [wl.S - 2, 1, 1]
     m = bench.kernel_model(wl, counts, 2)
     H, I, T = wl.H, wl.I, wl.T
-    assert m["gate_up_glu"][0] == 3 * 2 * I * H * 2 + T * H * 2
-    assert m["down_weighted"][0] == 3 * H * I * 2
-    assert m["down_dgrad_glu_bwd"][0] == 3 * H * I * 2 + T * H * 2
-    assert m["gate_up_dgrad"][0] == 3 * 2 * I * H * 2
-    assert bench.roofline_for("gate_up_glu", 1.0, m)["bound"] == "mfma"   # 3 experts' weights, 16384 slots
+
+    def both(name):   # the hot expert runs on the 256-row tiles, the other two on the small ones
+        return m[name][0] + m[name + "_big"][0]
+    assert both("gate_up_glu") == pytest.approx(3 * 2 * I * H * 2 + T * H * 2)
+    assert both("down_weighted") == 3 * H * I * 2
+    assert both("down_dgrad_glu_bwd") == pytest.approx(3 * H * I * 2 + T * H * 2)
+    assert both("gate_up_dgrad") == 3 * 2 * I * H * 2
+    assert bench.roofline_for("gate_up_glu_big", 1.0, m)["bound"] == "mfma"   # 1 expert's weights, 16382 slots
     spread = bench.kernel_model(wl, np.full(wl.E, wl.S // wl.E, dtype=np.int64), 2)
     rf = bench.roofline_for("gate_up_glu", 1.0, spread)
     assert rf["bound"] == "hbm"            # every expert's weights for ~128 slots each: weight-stream bound
@@ -64,7 +67,7 @@ def test_projection_bytes_are_weights_and_layer_inputs():
     zipf = WORKLOADS["zipf"]
     zc = np.full(zipf.E, zipf.S // zipf.E, dtype=np.int64)
     mz = bench.kernel_model(zipf, zc, 2)
-    rz = bench.roofline_for("gate_up_glu", 2.0, mz)
+    rz = bench.roofline_for("gate_up_glu_big", 2.0, mz)   # 1024 slots per expert: the 256-row tiles
     assert rz["bound"] == "mfma" and rz["achieved"] == pytest.approx(4.0 * zipf.S * H * I / 2e-3 / 1e12, rel=1e-3)
 
 
@@ -81,3 +84,32 @@ def test_fp32_operands_use_one_entry():
     counts = np.array([300, 250, 50, 0])
     m = bench.kernel_model(wl, counts, 4)
     assert "wgrad_gate_up_hot" not in m and m["wgrad_gate_up"][1] == pytest.approx(4.0 * 600 * 64 * 32)
+
+
+def test_token_row_split_by_tile_engine():
+    """With bf16 operands and H, I multiples of 32, experts of at least
+    LARGE_MIN slots are charged to the 256-row kernels (*_big), the rest to
+    the 128/192-row ones; flops and weights split by expert exactly and the
+    layer's input rows are charged once in total."""
+    wl = WORKLOADS["zipf"]
+    rng = np.random.default_rng(3)
+    counts = rng.integers(0, 2 * bench.LARGE_MIN, size=wl.E).astype(np.int64)
+    counts[0] = bench.LARGE_MIN          # at the limit: large tiles
+    counts[1] = bench.LARGE_MIN - 1      # just below: small tiles
+    counts[2] = 0
+    counts[-1] += wl.S - counts.sum()    # make the slots add up to S
+    assert counts[-1] >= 0
+    m = bench.kernel_model(wl, counts, 2)
+    H, I, T, S = wl.H, wl.I, wl.T, wl.S
+    big = counts >= bench.LARGE_MIN
+    for name, per_flop, w_rows, x_rows in [("gate_up_glu", 4.0, 2 * I * H, True), ("down_weighted", 2.0, H * I, False),
+                                           ("down_dgrad_glu_bwd", 2.0, H * I, True), ("gate_up_dgrad", 4.0, 2 * I * H, False)]:
+        assert m[name + "_big"][1] == pytest.approx(per_flop * counts[big].sum() * H * I)
+        assert m[name][1] + m[name + "_big"][1] == pytest.approx(per_flop * S * H * I)
+        touched = int((counts > 0).sum())
+        total = m[name][0] + m[name + "_big"][0]
+        assert total == pytest.approx(touched * w_rows * 2 + (T * H * 2 if x_rows else 0))
+    # H not a multiple of 32: one entry per product
+    odd = Workload("odd", 4096, 264, 200, 8, 1, "bf16", "swiglu", "concat")
+    m2 = bench.kernel_model(odd, np.array([4000, 96, 0, 0, 0, 0, 0, 0]), 2)
+    assert "gate_up_glu_big" not in m2 and m2["gate_up_glu"][1] == pytest.approx(4.0 * 4096 * 264 * 200)
