@@ -261,10 +261,13 @@ struct NLoader {
 // Configs whose MN-contiguous A tile is 256 columns wide, held as two
 // [k][128] halves (see the long-K weight gradient).
 template <class C> struct WideA { static constexpr bool value = false; };
+// 256-column N tiles (bf16): the MN-contiguous B tile is two [k][128] halves too
+// (NLoader2); only B is MN-contiguous in the kernels that use them.
+template <class C> constexpr bool kWideMN = WideA<C>::value || C::BN == 256;
 
 template <class C>
 __device__ __forceinline__ bf16x8_t frag_n(const typename C::elem* tile, int cb, int kk, int lane) {
-  if constexpr (WideA<C>::value) {   // columns 128.. live in the second [k][128] half
+  if constexpr (kWideMN<C>) {   // columns 128.. live in the second [k][128] half
     tile += (cb >> 7) * 128 * C::BK;
     cb &= 127;
   }
@@ -500,10 +503,39 @@ __device__ __forceinline__ void mainloop(AL& al, BL& bl, ALoadFn aload, BLoadFn 
   const int wm = wave / C::WN, wn = wave % C::WN;                          \
   (void)lane; (void)wm; (void)wn;
 
+// Two NLoaders for a 256-column MN-contiguous tile, held as two [k][128]
+// halves (128 x 256 token-row tiles); the second half's columns start 128
+// after the first's, and its rows past the valid columns load in range and
+// are masked to zero like the first's.
+template <class C, int ROT>
+struct NLoader2 {
+  using T = typename C::elem;
+  NLoader<C, ROT> h0;
+  NLoader<C, (ROT + C::NT / 4) % C::NT> h1;
+  static constexpr int NI = 2 * NLoader<C, ROT>::NI;
+  static constexpr int WRITES = NI;
+  __device__ __forceinline__ void init(int mn_valid, int kvalid) {
+    h0.init(mn_valid, kvalid);
+    h1.init(mn_valid - 128, kvalid);
+  }
+  template <int SET, class KRow>
+  __device__ __forceinline__ void load(int kt, KRow krow) {
+    h0.template load<SET>(kt, krow);
+    h1.template load<SET>(kt, [&](int k) { return krow(k) + 128; });
+  }
+  template <int SET>
+  __device__ __forceinline__ void store(T* lds) {
+    h0.template store<SET>(lds);
+    h1.template store<SET>(lds + 128 * C::BK);
+  }
+};
+
 // MN-contiguous operands: rows of k in LDS read with transposing LDS reads for
 // bf16, an in-register transpose for fp32.
 template <class C, int ROT>
-using MNLoader = std::conditional_t<sizeof(typename C::elem) == 2, NLoader<C, ROT>, TransLoader<C, 128, ROT>>;
+using MNLoader = std::conditional_t<sizeof(typename C::elem) == 2,
+                                    std::conditional_t<C::BN == 256, NLoader2<C, ROT>, NLoader<C, ROT>>,
+                                    TransLoader<C, 128, ROT>>;
 template <class C> constexpr bool kNLayout = sizeof(typename C::elem) == 2;
 
 // bf16 operands fit the two-set pipeline in 256 registers when a wave's
@@ -1478,6 +1510,7 @@ static bool use_bm256(const GemmProblem& pb) {
   return pb.dtype == 0 && mean >= 320;
 }
 using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
+using CfgBW = Cfg<uint16_t, 128, 256, 64, 2, 4>;  // bf16, 128 x 256 on 8 waves
 // weight gradients (one persistent workgroup per CU: operands, staging tile and tables in LDS)
 using CfgWB = Cfg<uint16_t, 128, 128, 64, 2, 4>;
 using CfgWF = Cfg<float, 128, 128, 16, 2, 2>;
@@ -1520,7 +1553,7 @@ hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu,
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
     return use_bm192(pb) ? gate_up_dispatch<CfgB192>(ps, X, Wgu, a_out, z_out, s)
-                         : gate_up_dispatch<CfgB>(ps, X, Wgu, a_out, z_out, s);
+                         : gate_up_dispatch<CfgBW>(ps, X, Wgu, a_out, z_out, s);
   }
   if (use_bm256(pb)) return gate_up_dispatch<CfgB256>(pb, X, Wgu, a_out, z_out, s);
   return use_bm192(pb) ? gate_up_dispatch<CfgB192>(pb, X, Wgu, a_out, z_out, s)
@@ -1543,13 +1576,15 @@ hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, voi
     const hipError_t e = dma_down(pb, a, Wd, Yp, s);
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
-    return use_bm192(pb) ? down_impl<CfgB192>(ps, a, Wd, Yp, s) : down_impl<CfgB>(ps, a, Wd, Yp, s);
+    return use_bm192(pb) ? down_impl<CfgB192>(ps, a, Wd, Yp, s) : down_impl<CfgBW>(ps, a, Wd, Yp, s);
   }
   if (use_bm256(pb)) return down_impl<CfgB256>(pb, a, Wd, Yp, s);
   return use_bm192(pb) ? down_impl<CfgB192>(pb, a, Wd, Yp, s) : down_impl<CfgB>(pb, a, Wd, Yp, s);
 }
 
-int down_dgrad_nparts(int I) { return (I + 127) / 128; }   // every down dgrad config uses BN = 128
+// Routing-weight partials of the down dgrad: one per 128 columns of I, for
+// every tile width (a 256-column tile writes two).
+int down_dgrad_nparts(int I) { return (I + 127) / 128; }
 
 template <class C>
 static hipError_t down_dgrad_impl(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ,
@@ -1557,7 +1592,7 @@ static hipError_t down_dgrad_impl(const GemmProblem& pb, const void* dY, const v
   GArgs g = base_args(pb, C::BM);
   g.A = dY; g.B = Wd; g.Z = Z; g.out0 = dZ; g.out1 = aw; g.partials = partials;
   g.ntn = (pb.I + C::BN - 1) / C::BN;
-  g.nparts = g.ntn;
+  g.nparts = down_dgrad_nparts(pb.I);   // one partial per 128 columns, BN / 128 per tile
   const long grid = row_grid(pb, C::BM, g.ntn);
   return run_kernel("down_dgrad_glu_bwd", s, [&] { down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
@@ -1575,7 +1610,7 @@ hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* 
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
     return use_bm192(pb) ? down_dgrad_impl<CfgB192>(ps, dY, Wd, Z, dZ, aw, partials, s)
-                         : down_dgrad_impl<CfgB>(ps, dY, Wd, Z, dZ, aw, partials, s);
+                         : down_dgrad_impl<CfgBW>(ps, dY, Wd, Z, dZ, aw, partials, s);
   }
   return use_bm192(pb) ? down_dgrad_impl<CfgB192>(pb, dY, Wd, Z, dZ, aw, partials, s)
                        : down_dgrad_impl<CfgB>(pb, dY, Wd, Z, dZ, aw, partials, s);
@@ -1603,7 +1638,7 @@ hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const voi
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
     return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(ps, dZ, Wgu, dXp, s)
-                         : gate_up_dgrad_impl<CfgB>(ps, dZ, Wgu, dXp, s);
+                         : gate_up_dgrad_impl<CfgBW>(ps, dZ, Wgu, dXp, s);
   }
   if (use_bm256(pb)) return gate_up_dgrad_impl<CfgB256>(pb, dZ, Wgu, dXp, s);
   return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(pb, dZ, Wgu, dXp, s)
