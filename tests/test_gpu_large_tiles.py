@@ -86,3 +86,22 @@ def test_large_tile_weight_grads_separate(layout):
     maps to rows of both tensors (interleaved) or straddles the boundary
     between them at I = 1056 (concatenated)."""
     check_separate(weight_grad_inputs(layout, 63), "swiglu", layout, "bf16", "bf16", True)
+
+
+@pytest.mark.parametrize("act,layout", [("clamped", "interleaved"), ("swiglu", "concat")])
+@pytest.mark.parametrize("save", [True, False])
+def test_small_experts_with_large_tile_shapes(act, layout, save):
+    """Experts below 512 slots with H and I multiples of 32 (the large-tile
+    engine enabled but finding no expert of its own): 192-row tiles when the
+    batch averages 101-176 slots per expert (here 116), 128 x 256 tiles above
+    that (the large-tile tests above, mean 505).  N is ragged in every
+    product (gate_up 320 dZ columns, down 288, gate_up dgrad 288, down dgrad
+    160); experts of 1-290 slots span one or two M-tiles."""
+    counts = [290, 193, 192, 150, 60, 1, 10]
+    E, K = len(counts), 1
+    T = sum(counts)
+    assert 101 <= T // E <= 176
+    rng = np.random.default_rng(71)
+    ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
+    inp = small_inputs(T, H, I, E, K, "bf16", act, layout, seed=71, ids=ids)
+    run_and_compare(inp, save=save, grad_dtype="bf16", poison=True)
