@@ -518,6 +518,10 @@ struct NLoader2 {
     h0.init(mn_valid, kvalid);
     h1.init(mn_valid - 128, kvalid);
   }
+  __device__ __forceinline__ void retarget(int mn_valid, int kvalid) {
+    h0.retarget(mn_valid, kvalid);
+    h1.retarget(mn_valid - 128, kvalid);
+  }
   template <int SET, class KRow>
   __device__ __forceinline__ void load(int kt, KRow krow) {
     h0.template load<SET>(kt, krow);
@@ -924,7 +928,7 @@ __global__ __launch_bounds__(C::NT + kStoreThreads, 1) void wgrad_kernel(GArgs g
   // ---------------- MMA waves
   const int lane = threadIdx.x & 63;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  MNLoader<C, 0> al;
+  std::conditional_t<WideA<C>::value, NLoader2<C, 0>, MNLoader<C, 0>> al;   // 256 columns of M: two halves
   MNLoader<C, C::NT / 2> bl;
   al.init(M - cur.m0, cur.cnt);
   bl.init(N - cur.n0, cur.cnt);
@@ -1513,6 +1517,12 @@ using CfgF = Cfg<float, 128, 128, 32, 2, 2>;      // fp32
 using CfgBW = Cfg<uint16_t, 128, 256, 64, 2, 4>;  // bf16, 128 x 256 on 8 waves
 // weight gradients (one persistent workgroup per CU: operands, staging tile and tables in LDS)
 using CfgWB = Cfg<uint16_t, 128, 128, 64, 2, 4>;
+// bf16 gradients of the tiled kernel: 256 x 128 tiles (8 waves of 64 x 64,
+// BK = 32 to leave LDS for the 64 KB staging tile), the 256 columns of M
+// held as two [k][128] halves: a quarter fewer operand bytes per flop than
+// 128 x 128.
+struct CfgWB256 : Cfg<uint16_t, 256, 128, 32, 4, 2> {};
+template <> struct WideA<CfgWB256> { static constexpr bool value = true; };
 using CfgWF = Cfg<float, 128, 128, 16, 2, 2>;
 
 template <class C, bool A, bool Z>
@@ -1738,7 +1748,7 @@ static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const voi
     const hipError_t e = pb.gdtype == 0 ? wgrad_res_impl<GU, uint16_t>(pb, A, B, dW, s)
                                         : wgrad_res_impl<GU, float>(pb, A, B, dW, s);
     if (e != hipSuccess) return e;
-    const hipError_t e2 = pb.gdtype == 0 ? wgrad_impl<CfgWB, GU, uint16_t>(pb, A, B, dW, s, kResKmax, kLongMin)
+    const hipError_t e2 = pb.gdtype == 0 ? wgrad_impl<CfgWB256, GU, uint16_t>(pb, A, B, dW, s, kResKmax, kLongMin)
                                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax, kLongMin);
     if (e2 != hipSuccess) return e2;
     if (dma_wgrad_enabled(pb)) return dma_wgrad(pb, GU, A, B, dW, kLongMin, s);
