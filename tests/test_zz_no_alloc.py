@@ -30,10 +30,11 @@ def test_noalloc_rejects_shapes_beyond_the_scratch_array():
                                None) == _lib.MOE_ERR_INVALID_ARG
 
 
-def _inputs(T, H, I, E, K, seed, dev="cuda"):
+def _inputs(T, H, I, E, K, seed, dev="cuda", hot=0.0):
     g = torch.Generator(device="cpu").manual_seed(seed)
     X = torch.randn(T, H, generator=g).to(torch.bfloat16).to(dev)
     logits = torch.randn(T, E, generator=g)
+    logits[:, 0] += hot   # hot > 0: expert 0 takes (nearly) every token
     top = torch.topk(logits, K, dim=1)
     ids = top.indices.to(torch.int32).to(dev)
     w = torch.softmax(top.values, dim=1).to(torch.float32).to(dev)
@@ -46,8 +47,13 @@ def _inputs(T, H, I, E, K, seed, dev="cuda"):
 @pytest.mark.parametrize("act,layout", [("clamped", "interleaved"), ("swiglu", "concat")])
 def test_noalloc_forward_equals_moe_fwd(act, layout):
     H, I, E, K = 1024, 512, 16, 4
-    for T, seed in [(700, 1), (96, 2)]:   # two calls in a row, the second smaller
-        X, ids, w, Wgu, Wd = _inputs(T, H, I, E, K, seed)
+    # calls in a row, each smaller than the one before; the first gives expert
+    # 0 every token (900 slots: the 256 x 256-tile kernels), the others
+    # spread the slots (the 128-row tiles only)
+    for T, seed, hot in [(900, 3, 50.0), (700, 1, 0.0), (96, 2, 0.0)]:
+        X, ids, w, Wgu, Wd = _inputs(T, H, I, E, K, seed, hot=hot)
+        if hot:
+            assert int((ids == 0).sum()) >= 512
         kw = dict(act=act, layout=layout)
         ref, ref_saved, ws = moe.fwd(X, ids, w, Wgu, Wd, save=True, **kw)
         sbytes = moe.workspace_size(moe.make_desc(T, H, I, E, K, "bf16", act, layout))[2]
