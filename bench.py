@@ -108,6 +108,22 @@ LONG_MIN = 512  # experts with more positions take the long-K weight gradient
 LARGE_MIN = 512  # experts with at least this many slots take the 256-row token-row tiles
 
 
+def large_tile_experts(wl, counts):
+    """Experts the library runs on the 256-row tiles: from LARGE_MIN slots on,
+    and below that those whose 256-row tiles hold no more rows than the other
+    engine's tiles (192 rows when the batch averages 101-176 slots per
+    expert, else 128) would."""
+    import numpy as np
+    counts = np.asarray(counts)
+    if not large_tiles(wl):
+        return np.zeros(len(counts), dtype=bool)
+    mean = wl.S // wl.E if wl.E else 0
+    bms = 192 if 100 < mean <= 176 else 128
+    rows_big = (counts + 255) // 256 * 256
+    rows_small = (counts + bms - 1) // bms * bms
+    return (counts >= LARGE_MIN) | ((counts > 0) & (rows_big <= rows_small))
+
+
 def large_tiles(wl):
     """Whether the library runs the 256 x 256-tile engine for this workload's
     big experts (bf16 operands, H and I multiples of 32, offsets in range)."""
@@ -150,7 +166,7 @@ def kernel_model(wl, counts, grad_bytes):
         m["gate_up_dgrad" + suffix] = (Wgu, 4.0 * s_part * H * I)
     import numpy as np
     counts = np.asarray(counts)
-    big = (counts >= LARGE_MIN) if large_tiles(wl) else np.zeros(len(counts), dtype=bool)
+    big = large_tile_experts(wl, counts)
     rows(~big, "")
     if big.any():
         rows(big, "_big")

@@ -84,6 +84,7 @@ RouteState route_state(void* ws, const Layout& L, const Dims& d) {
   rs.w_of_pos = (float*)(b + L.w_of_pos);
   rs.nblk = d.nblk;
   rs.big_min = 0x7fffffff;   // no large-tile experts unless the GEMM problem allows them
+  rs.small_bm = 128;
   return rs;
 }
 
@@ -332,6 +333,7 @@ static moe_status_t fwd_impl(const moe_desc_t* desc, const void* hidden, const i
     pb.layout = 0;   // Z columns: gate then up
   }
   rs.big_min = large_tile_min_slots(pb);
+  rs.small_bm = small_tile_rows(pb);
   char* b = (char*)ws;
   void* a = b + L.f_a;
   float* yp = (float*)(b + L.f_y);
@@ -384,6 +386,7 @@ static moe_status_t bwd_impl(const moe_desc_t* desc, const void* hidden, const i
     pb.layout = 0;   // Z and dZ columns: gate then up
   }
   rs.big_min = large_tile_min_slots(pb);
+  rs.small_bm = small_tile_rows(pb);
   char* b = (char*)ws;
   void* z = b + L.b_z;
   void* dz = b + L.b_dz;

@@ -1502,6 +1502,7 @@ static bool use_bm192(const GemmProblem& pb) {
   const long mean = pb.E > 0 ? (long)pb.S / pb.E : 0;
   return pb.dtype == 0 && mean > 100 && mean <= 176;
 }
+int small_tile_rows(const GemmProblem& pb) { return use_bm192(pb) ? 192 : 128; }
 // bf16 with 256x128 tiles on 8 waves (64x64 each, one workgroup per CU):
 // when experts average several hundred positions, a quarter fewer operand
 // bytes per flop from L2 than 128x128 tiles (Zipf workload: gate_up 6.42 ->
@@ -1545,8 +1546,8 @@ static hipError_t gate_up_dispatch(const GemmProblem& pb, const void* X, const v
 }
 
 // With the large-tile engine on, a token-row GEMM runs as two launches: the
-// experts with at least rs->big_min slots in 256 x 256 tiles (gemm_dma.hip),
-// then the others in this engine's 128-row tiles (192-row when experts
+// large-tile experts (large_tile_expert) in 256 x 256 tiles (gemm_dma.hip),
+// then the others in this engine's 128 x 256 tiles (192 x 128 when experts
 // average 101-176 slots), each over its own tile table.
 static GemmProblem small_experts(const GemmProblem& pb) {
   GemmProblem p = pb;

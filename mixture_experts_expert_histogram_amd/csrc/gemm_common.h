@@ -375,7 +375,7 @@ __device__ __forceinline__ void epi_gate_up_dgrad(const GArgs& g, f32x16 (&acc)[
 
 // ------------------------------------------------------------------ host side
 // Large-tile engine (gemm_dma.hip): bf16 operands, H and I multiples of 32;
-// each launch covers the experts with at least rs->big_min slots.
+// each launch covers the large-tile experts (large_tile_expert).
 bool dma_enabled(const GemmProblem& pb);
 hipError_t dma_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
                        hipStream_t s);

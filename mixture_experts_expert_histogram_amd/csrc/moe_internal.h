@@ -12,16 +12,25 @@ constexpr int ROUTE_CHUNK = 512;
 constexpr int MAX_E = 1024;
 // Tile prefix tables the routing scan writes, one per (M-tile height, set of
 // experts): tables 0-4 cover every expert with 32, 64, 128, 256 and 192-row
-// tiles; table 5 covers the experts with at least big_min slots in 256-row
-// tiles (the large-tile engine), tables 6 and 7 the experts below it in 128
-// and 192-row tiles.
+// tiles; table 5 covers the large-tile experts (large_tile_expert) in
+// 256-row tiles, tables 6 and 7 the others in 128 and 192-row tiles.
 constexpr int N_TILE_TABLES = 8;
 constexpr int TILE_BIG256 = 5, TILE_SMALL128 = 6, TILE_SMALL192 = 7;
 __host__ __device__ constexpr int tile_bm(int j) {
   return j < 4 ? 32 << j : j == 4 ? 192 : j == TILE_BIG256 ? 256 : j == TILE_SMALL128 ? 128 : 192;
 }
-// 0: every expert, 1: experts with at least big_min slots, 2: the others
+// 0: every expert, 1: the large-tile experts, 2: the others
 __host__ __device__ constexpr int tile_set(int j) { return j < 5 ? 0 : j == TILE_BIG256 ? 1 : 2; }
+
+// Whether an expert of c slots runs on the large-tile engine's 256-row tiles:
+// from big_min slots on, and below that when its 256-row tiles hold no more
+// rows than the small_bm-row tiles of the other engine would (with 128-row
+// tiles 129-256 and 385-511 slots, with 192-row tiles 193-256 and 385-511):
+// the same rows on the faster engine.  big_min = INT_MAX: none.
+__host__ __device__ constexpr bool large_tile_expert(int c, int big_min, int small_bm) {
+  return c >= big_min ||
+         (big_min != 0x7fffffff && c > 0 && (c + 255) / 256 * 256 <= (c + small_bm - 1) / small_bm * small_bm);
+}
 
 // Device views of the routing state that lives in the workspace.
 struct RouteState {
@@ -38,6 +47,7 @@ struct RouteState {
   float* w_of_pos;        // [S] routing weight of the slot at each position
   int nblk;
   int big_min;            // experts with at least this many slots use the large-tile engine
+  int small_bm;           // M-tile rows of the other engine (128 or 192), for large_tile_expert
 };
 
 // Host side: optional timing events around each kernel launch (api.cpp).
@@ -84,8 +94,8 @@ struct GemmProblem {
   // (layout is then the concatenated one for Z and dZ); null when fused
   const void* w_up = nullptr;
   void* dw_up = nullptr;
-  // experts a token-row launch covers: 0 all, 1 those with at least
-  // rs->big_min slots (large-tile engine), 2 the others
+  // experts a token-row launch covers: 0 all, 1 the large-tile experts
+  // (large_tile_expert), 2 the others
   int tile_set = 0;
 };
 // Per-slot buffers are indexed by the expert-sorted position p.
@@ -112,6 +122,8 @@ hipError_t launch_wgrad_gate_up(const GemmProblem& pb, const void* dZ, const voi
 // token-row GEMM of the problem (INT_MAX: none); set in the routing state
 // before routing.
 int large_tile_min_slots(const GemmProblem& pb);
+// M-tile rows of the small-tile engine for the other experts (128 or 192).
+int small_tile_rows(const GemmProblem& pb);
 
 // rows dst[p] = src[tok_of_pos[p]] of width `row_bytes` (a multiple of 16)
 hipError_t launch_gather_rows(const void* src, const int32_t* tok_of_pos, int S, size_t row_bytes, void* dst,

@@ -57,7 +57,8 @@ __device__ int block_exclusive_scan_1024(int v, int* sh) {
 
 // Pass 2 (one workgroup): counts, offsets, per-chunk bases, M-tile tables,
 // the bad-id flag, and the experts ordered by descending count.
-__global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int big_min, int32_t* __restrict__ blk_hist,
+__global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int big_min, int small_bm,
+                                                          int32_t* __restrict__ blk_hist,
                                                           int32_t* __restrict__ blk_bad,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int b
   }
   for (int j = 0; j < N_TILE_TABLES; ++j) {
     const int bm = tile_bm(j), set = tile_set(j);
-    const bool in = set == 0 || (set == 1) == (c >= big_min);
+    const bool in = set == 0 || (set == 1) == large_tile_expert(c, big_min, small_bm);
     const int nt = (e < E && in) ? (c + bm - 1) / bm : 0;
     const int p = block_exclusive_scan_1024(nt, sh);
     if (e < E) tile_prefix[j * (E + 1) + e] = p;
@@ -310,7 +311,8 @@ hipError_t launch_route(const int32_t* ids, const float* w, int S, int K, int E,
   });
   if (err != hipSuccess) return err;
   err = run_kernel("route_scan", stream, [&] {
-    route_scan_kernel<<<1, 1024, 0, stream>>>(nblk, E, rs.big_min, rs.blk_hist, rs.blk_bad, rs.counts, rs.offsets,
+    route_scan_kernel<<<1, 1024, 0, stream>>>(nblk, E, rs.big_min, rs.small_bm, rs.blk_hist, rs.blk_bad, rs.counts,
+                                              rs.offsets,
                                               rs.tile_prefix, rs.expert_order, rs.status);
   });
   if (err != hipSuccess) return err;

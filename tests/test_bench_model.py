@@ -87,21 +87,24 @@ def test_fp32_operands_use_one_entry():
 
 
 def test_token_row_split_by_tile_engine():
-    """With bf16 operands and H, I multiples of 32, experts of at least
-    LARGE_MIN slots are charged to the 256-row kernels (*_big), the rest to
-    the 128/192-row ones; flops and weights split by expert exactly and the
-    layer's input rows are charged once in total."""
+    """With bf16 operands and H, I multiples of 32, the large-tile experts
+    (LARGE_MIN slots and more, and smaller ones whose 256-row tiles hold no
+    more rows than 128-row tiles would) are charged to the 256-row kernels
+    (*_big), the rest to the small-tile ones; flops and weights split by
+    expert exactly and the layer's input rows are charged once in total."""
     wl = WORKLOADS["zipf"]
     rng = np.random.default_rng(3)
     counts = rng.integers(0, 2 * bench.LARGE_MIN, size=wl.E).astype(np.int64)
     counts[0] = bench.LARGE_MIN          # at the limit: large tiles
-    counts[1] = bench.LARGE_MIN - 1      # just below: small tiles
+    counts[1] = 300                      # 512 rows of 256-row tiles against 384 of 128-row ones: small tiles
     counts[2] = 0
+    counts[3] = 200                      # one 256-row tile against two 128-row ones: large tiles
     counts[-1] += wl.S - counts.sum()    # make the slots add up to S
     assert counts[-1] >= 0
     m = bench.kernel_model(wl, counts, 2)
     H, I, T, S = wl.H, wl.I, wl.T, wl.S
-    big = counts >= bench.LARGE_MIN
+    big = bench.large_tile_experts(wl, counts)
+    assert big[0] and not big[1] and not big[2] and big[3]
     for name, per_flop, w_rows, x_rows in [("gate_up_glu", 4.0, 2 * I * H, True), ("down_weighted", 2.0, H * I, False),
                                            ("down_dgrad_glu_bwd", 2.0, H * I, True), ("gate_up_dgrad", 4.0, 2 * I * H, False)]:
         assert m[name + "_big"][1] == pytest.approx(per_flop * counts[big].sum() * H * I)
@@ -113,3 +116,21 @@ def test_token_row_split_by_tile_engine():
     odd = Workload("odd", 4096, 264, 200, 8, 1, "bf16", "swiglu", "concat")
     m2 = bench.kernel_model(odd, np.array([4000, 96, 0, 0, 0, 0, 0, 0]), 2)
     assert "gate_up_glu_big" not in m2 and m2["gate_up_glu"][1] == pytest.approx(4.0 * 4096 * 264 * 200)
+
+
+@pytest.mark.parametrize("bms", [128, 192])
+def test_large_tile_rule_rows(bms):
+    """The rule takes an expert to the 256-row tiles exactly when its rows
+    padded to 256 do not exceed its rows padded to the small tile (brute
+    force over 1..600 slots)."""
+    mean = 150 if bms == 192 else 400
+    wl = Workload("rule", mean * 8, 2880, 2880, 8, 1, "bf16", "swiglu", "concat")
+    c = np.arange(0, 601)
+    got = bench.large_tile_experts(wl, c)
+    for n in range(0, 601):
+        want = n >= bench.LARGE_MIN or (n > 0 and -(-n // 256) * 256 <= -(-n // bms) * bms)
+        assert got[n] == want, n
+    if bms == 128:
+        assert got[129] and got[256] and not got[257] and not got[384] and got[385] and not got[128]
+    else:
+        assert not got[192] and got[193] and got[256] and not got[257] and got[385]
