@@ -130,6 +130,8 @@ def large_tiles(wl):
     lim = 1 << 31
     return (wl.dtype == "bf16" and wl.H % 32 == 0 and wl.I % 32 == 0 and wl.T * wl.H * 2 < lim
             and 4 * wl.I * wl.H < lim and 256 * 4 * wl.I < lim and 256 * 2 * wl.H < lim)
+
+
 def kernel_model(wl, counts, grad_bytes):
     """Algorithmic bytes and routed flops of one launch of each kernel.
 

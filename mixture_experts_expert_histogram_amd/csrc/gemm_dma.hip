@@ -6,36 +6,40 @@
 // those experts this engine computes 256 x 256 tiles on 8 waves (2 x 4,
 // 128 x 64 per wave) of v_mfma_f32_32x32x16_bf16, with both operands moved
 // from global memory straight into LDS by global_load_lds_dwordx4 (no staging
-// registers, no ds_write), through a ring of five LDS stages of BK = 32 (all
-// 160 KB of LDS):
+// registers, no ds_write), through a ring of LDS stages: two of BK = 64
+// (128 KB) in the token-row kernels when H and I are multiples of 64, five
+// of BK = 32 (all 160 KB of LDS) otherwise and in the weight gradients:
 //
 // * Ping-pong: the two row halves of waves (one wave of each per SIMD) run
-//   half a step apart, so on every SIMD one wave issues MFMAs while the other
-//   refills a stage and reads its fragments (pp_step).
-// * Every step starts with a wait for the wave's own loads of that step
-//   (vmcnt; three steps of loads stay in flight) and a plain s_barrier;
-//   __syncthreads() would also wait for every load in flight.
-// * The five stages are five distinct __shared__ arrays, the ring is unrolled
-//   by five and every refill is issued unconditionally (clamped to the last
-//   step), so the wait counts are constants.
+//   half a 32-k sub-step apart, so on every SIMD one wave issues MFMAs while
+//   the other refills a stage and reads its fragments (pp_step).
+// * Every stage starts with a wait for the wave's own loads of that stage
+//   (vmcnt; NSTAGE - 2 stages of loads stay in flight) and a plain
+//   s_barrier; __syncthreads() would also wait for every load in flight.
+// * The stages are distinct __shared__ arrays, the ring is unrolled by its
+//   length and every refill is issued unconditionally (clamped to the last
+//   stage), so the wait counts are constants.
 // * A load writes 64 lanes x 16 bytes to consecutive LDS bytes; the tiles'
 //   XOR swizzles come from permuting which 16 bytes of global memory each
 //   lane reads (no LDS bank conflicts, measured).
 //
 // Measured limits (rocprofv3 counters on the Zipf batch): the token-row
 // kernels keep the texture data path that feeds LDS 86-94 % busy at about
-// half the MFMA rate; with 64-byte row segments per load (k-contiguous
-// operands, BK = 32) it moves about 17 bytes per clock and CU.  Probes with
-// 128-byte segments (BK = 64, two stages, 4 waves of 128 x 128) move 28 but
-// stall elsewhere and land at the same throughput; hipBLASLt reaches about
-// 1.35 PFLOP/s on a plain 24576 x 5632 x 2880 product against about 1.0 here.
+// half the MFMA rate.  It moves about 17 bytes per clock and CU with 64-byte
+// row segments per load (k-contiguous operands at BK = 32) and about 28 with
+// 128-byte ones (BK = 64), which is what the 64-k stages are for: the Zipf
+// batch's token-row kernels ran 5-8 % faster on them than on the five 32-k
+// stages, despite loads issued only one stage ahead.  hipBLASLt reaches
+// about 1.35 PFLOP/s on a plain 24576 x 5632 x 2880 product against about
+// 1.0 here.
 //
-// Operands contiguous along k are [row][32] tiles (64-byte rows, 16-byte
-// chunks XORed with (row / 4) % 4); operands contiguous along m or n (the
-// weights of the input gradients, both operands of the weight gradients) are
-// [32][128] column halves read with ds_read_b64_tr_b16, like the other
-// engine's.  K must be a multiple of 32 (the weight gradients' ragged k is
-// handled by clamped rows and zeroed LDS rows).
+// Operands contiguous along k are [row][BK] tiles (16-byte chunks XORed
+// with (row / 4) % 4 for 64-byte rows, (row / 2) % 8 for 128-byte ones);
+// operands contiguous along m or n (the weights of the input gradients, both
+// operands of the weight gradients) are [BK][128] column halves read with
+// ds_read_b64_tr_b16, like the other engine's.  K must be a multiple of BK
+// (the weight gradients' ragged k is handled by clamped rows and zeroed LDS
+// rows).
 #include "gemm_common.h"
 
 namespace moe {
@@ -76,44 +80,59 @@ __device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint16
       : "memory", "m0");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int NSTAGE_ = 4>
+// BK = 32 or 64 k per stage.  With 64, a k-contiguous operand's load covers
+// 8 rows x 128 bytes (whole cache lines) instead of 16 rows x 64 bytes; the
+// texture data path that returns the loads to LDS moves about 28 bytes per
+// clock and CU with whole lines and about 17 with half lines.  A stage of
+// 64 k is consumed in two 32-k sub-steps of the ping-pong schedule.
+template <int BM_, int BN_, int WM_, int WN_, int NSTAGE_ = 4, int BK_ = 32>
 struct DCfg {
   using elem = uint16_t;
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32, NSTAGE = NSTAGE_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NSTAGE = NSTAGE_;
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK, STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int NBA = BM / 16 / NW, NBB = BN / 16 / NW;   // 1 KB loads per wave and step
+  static constexpr int NBA = BM * BK * 2 / 1024 / NW, NBB = BN * BK * 2 / 1024 / NW;   // 1 KB loads per wave and stage
   static constexpr int PER = NBA + NBB;
-  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "whole 1 KB loads per wave");
+  static constexpr int SUB = BK / 32;   // 32-k sub-steps per stage
+  static_assert(BK == 32 || BK == 64, "stages of 32 or 64 k");
+  static_assert((BM * BK * 2) % (1024 * NW) == 0 && (BN * BK * 2) % (1024 * NW) == 0, "whole 1 KB loads per wave");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "column halves of 128");
 };
-using DCfgB = DCfg<256, 256, 2, 4, 5>;
+using DCfgB = DCfg<256, 256, 2, 4, 5>;         // 5 stages of 32 k (160 KB)
+using DCfgB64 = DCfg<256, 256, 2, 4, 2, 64>;   // 2 stages of 64 k (128 KB)
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt <= n and lgkmcnt = 0.
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-// Element offset of 16-byte chunk `chunk` (0..3) of row `row` in a [row][32]
-// tile: 16 lanes reading one chunk of 16 consecutive rows hit 16 bank groups.
-__device__ __forceinline__ int krow_off(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3); }
+// Swizzle of a [row][BK] k-contiguous tile: 16-byte chunk c of row r is
+// stored at slot c ^ kswz(r), so 16 lanes reading one chunk of 16
+// consecutive rows hit 16 bank groups (64-byte rows: (r / 4) % 4; 128-byte
+// rows: (r / 2) % 8).
+template <int BK>
+__device__ __forceinline__ int kswz(int row) { return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7; }
+template <int BK>
+__device__ __forceinline__ int krow_off(int row, int chunk) { return row * BK + ((chunk ^ kswz<BK>(row)) << 3); }
 
-// A k-contiguous operand: NB loads per wave per step, load j of wave w holds
-// tile rows (w * NB + j) * 16 .. +16; lane l reads 16 bytes of row
-// 16 b + l / 4, the chunk whose swizzled slot is l % 4.  A load's 16 rows
+// A k-contiguous operand: NB loads per wave per stage, load j of wave w
+// holds tile rows (w * NB + j) * RPL .. +RPL (RPL = 16 rows of 64 bytes at
+// BK = 32, 8 rows of 128 bytes at BK = 64); lane l reads 16 bytes of row
+// RPL b + l / LPR, the chunk whose swizzled slot is l % LPR.  A load's rows
 // share one scalar base (rows of one 32-row gate or up group).
-template <int NB>
+template <int NB, int BK = 32>
 struct RowSrc {
+  static constexpr int LPR = BK / 8, RPL = 64 / LPR;   // lanes per row, rows per load
   const char* base[NB];
   uint32_t off[NB];
   // rowsrc(r, base, off): tile row r (clamped by the caller) starts `off`
-  // bytes after `base`, which is the same for the 16 rows of a load
+  // bytes after `base`, which is the same for the RPL rows of a load
   template <class RowSrcFn>
   __device__ __forceinline__ void init(RowSrcFn rowsrc, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int row = (wave * NB + j) * 16 + (lane >> 2);
-      const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = (wave * NB + j) * RPL + lane / LPR;
+      const int chunk = (lane % LPR) ^ kswz<BK>(row);
       const char* b;
       uint32_t o;
       rowsrc(row, b, o);
@@ -123,24 +142,25 @@ struct RowSrc {
   }
   __device__ __forceinline__ void issue(int kt, uint16_t* tile, int wave) const {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) lds_dma16(base[j], off[j] + kt * 64, tile + (wave * NB + j) * 512);
+    for (int j = 0; j < NB; ++j) lds_dma16(base[j], off[j] + kt * (BK * 2), tile + (wave * NB + j) * 512);
   }
 };
 
 // An operand contiguous along m or n (k rows of columns): the tile is
-// [32 k][COLS] held as COLS / 128 halves of [32][128] (256-byte rows, chunks
-// XORed with 4 * (k % 4)); load b covers half b / 8, k rows 4 (b % 8) .. +4;
-// lane l reads 16 bytes of k row 4 (b % 8) + l / 16.  k rows below ksplit
-// are rows of base0, the others rows k - ksplit of base1 (ksplit a multiple
-// of 32, so a step takes one side); ld elements per row; columns past the
-// valid ones are clamped.
+// [BK k][COLS] held as COLS / 128 halves of [BK][128] (256-byte rows, chunks
+// XORed with 4 * (k % 4)); with KPH = BK / 4 loads per half, load b covers
+// half b / KPH, k rows 4 (b % KPH) .. +4; lane l reads 16 bytes of k row
+// 4 (b % KPH) + l / 16.  k rows below ksplit are rows of base0, the others
+// rows k - ksplit of base1 (ksplit a multiple of BK, so a stage takes one
+// side); ld elements per row; columns past the valid ones are clamped.
 //
 // CLAMP (the weight gradients, whose k is an expert's positions): k rows
 // past kmax read row kmax instead, so the ragged last step stays inside the
 // expert's rows; the kernel zeroes what those rows put into LDS where it
 // matters (dma_zero_rows).
-template <int NB, bool CLAMP = false>
+template <int NB, bool CLAMP = false, int BK = 32>
 struct ColSrc {
+  static constexpr int KPH = BK / 4;   // loads per 128-column half
   const char* b0;
   const char* b1;
   uint32_t off[NB];   // bytes from a step's first k row to this lane's 16 bytes (no CLAMP)
@@ -158,16 +178,16 @@ struct ColSrc {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int b = wave * NB + j;
-      const int krow = (b & 7) * 4 + (lane >> 4);
+      const int krow = (b % KPH) * 4 + (lane >> 4);
       const int chunk = (lane & 15) ^ ((krow & 3) << 2);
-      const int col = min(c0 + (b >> 3) * 128 + chunk * 8, ncols - 8);
+      const int col = min(c0 + (b / KPH) * 128 + chunk * 8, ncols - 8);
       off[j] = krow * row_bytes + col * 2;
       coff[j] = col * 2;
       kr[j] = krow;
     }
   }
   __device__ __forceinline__ void issue(int kt, uint16_t* tile, int wave) const {
-    const int k0 = kt * 32;
+    const int k0 = kt * BK;
     if constexpr (CLAMP) {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
@@ -182,23 +202,24 @@ struct ColSrc {
   }
 };
 
-// Zero the k rows from kvalid on that this wave's NB loads of a [32][COLS]
+// Zero the k rows from kvalid on that this wave's NB loads of a [BK][COLS]
 // column-half tile wrote (each lane its own 16 bytes), so rows past an
 // expert's last position add nothing.  The wave's own loads must have landed.
-template <int NB>
+template <int NB, int BK>
 __device__ __forceinline__ void dma_zero_rows(uint16_t* tile, int kvalid, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int b = wave * NB + j;
-    if ((b & 7) * 4 + (lane >> 4) >= kvalid) *(uint4*)(tile + b * 512 + lane * 8) = make_uint4(0, 0, 0, 0);
+    if ((b % (BK / 4)) * 4 + (lane >> 4) >= kvalid) *(uint4*)(tile + b * 512 + lane * 8) = make_uint4(0, 0, 0, 0);
   }
 }
 
 // 32 columns x 16 k of a [32][128]-half tile (columns from cb), in the
 // fragment layout of the k-contiguous reads: lane -> column cb + lane % 32,
 // k = kk * 16 + 8 (lane / 32) + 0..7.
+template <int BK>
 __device__ __forceinline__ bf16x8_t frag_cols(const uint16_t* tile, int cb, int kk, int lane) {
-  tile += (cb >> 7) * (32 * 128);
+  tile += (cb >> 7) * (BK * 128);
   cb &= 127;
   const int g = lane >> 4, s = lane & 15;
   const int col = cb + ((g & 1) << 4) + ((s & 3) << 2);
@@ -229,12 +250,12 @@ __device__ __forceinline__ void dma_read(const uint16_t* As, const uint16_t* Bs,
   const int r32 = lane & 31, chunk = kk * 2 + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
-    f.a[i] = A_MN ? frag_cols(As, wm * C::WTM + i * 32, kk, lane)
-                  : *(const bf16x8_t*)(As + krow_off(wm * C::WTM + i * 32 + r32, chunk));
+    f.a[i] = A_MN ? frag_cols<C::BK>(As, wm * C::WTM + i * 32, kk, lane)
+                  : *(const bf16x8_t*)(As + krow_off<C::BK>(wm * C::WTM + i * 32 + r32, chunk));
 #pragma unroll
   for (int j = 0; j < C::FN; ++j)
-    f.b[j] = B_MN ? frag_cols(Bs, wn * C::WTN + j * 32, kk, lane)
-                  : *(const bf16x8_t*)(Bs + krow_off(wn * C::WTN + j * 32 + r32, chunk));
+    f.b[j] = B_MN ? frag_cols<C::BK>(Bs, wn * C::WTN + j * 32, kk, lane)
+                  : *(const bf16x8_t*)(Bs + krow_off<C::BK>(wn * C::WTN + j * 32 + r32, chunk));
 }
 
 template <class C>
@@ -254,57 +275,77 @@ __device__ __forceinline__ void dma_issue(const AS& as, const BS& bs, int kt, ui
 }
 
 // Ping-pong schedule of the ring: the two row halves of waves (wm = 0, 1;
-// one wave of each on every SIMD) run half a step apart, so that on every
-// SIMD one wave issues MFMAs while the other reads fragments and issues
-// loads.  Every wave runs the same step (barrier, refill + reads, barrier,
-// MFMAs); the upper half passes one extra barrier first and the lower half
-// one at the end, so with barriers A_t, B_t of step t:
+// one wave of each on every SIMD) run half a sub-step apart, so that on
+// every SIMD one wave issues MFMAs while the other reads fragments and
+// issues loads.  A sub-step is 32 k (a stage of 64 k has two).  Every wave
+// runs the same sub-step (barrier, refill + reads, barrier, MFMAs); the
+// upper half passes one extra barrier first and the lower half one at the
+// end, so with barriers A_q, B_q of sub-step q:
 //
-//   after A_t:  wm = 0 refills and reads step t | wm = 1 MFMAs of step t-1
-//   after B_t:  wm = 0 MFMAs of step t          | wm = 1 refills and reads step t
+//   after A_q:  wm = 0 reads sub-step q (refills at a stage's first) | wm = 1 MFMAs of q-1
+//   after B_q:  wm = 0 MFMAs of sub-step q                            | wm = 1 reads q (refills ...)
 //
-// Before A_t every wave's own loads of step t have landed (the lower half
-// waits before A_t, the upper one after its reads of step t-1) and, with a
-// ragged k, its rows of A past klast are zeroed.  The stage refilled with
-// step t+3 was read in step t-1 by both halves, before A_t (the upper half
-// waits for its reads with the same wait).  Two steps of loads stay in
-// flight at each wait.
+// Before the A barrier of a stage's first sub-step every wave's own loads of
+// that stage have landed (the lower half waits before it, the upper one
+// after its reads of the previous sub-step) and, with a ragged k, its rows
+// of A past klast are zeroed.  The stage refilled with stage t+NS-1 was read
+// in stage t-1 by both halves, before that barrier (the upper half waits for
+// its reads with the same wait).  NS-2 stages of loads stay in flight at
+// each wait.
 template <class C, bool ZERO>
 __device__ __forceinline__ void pp_land(int kt, int last, uint16_t* St, int wave, int lane, int klast) {
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));   // own loads of step kt landed
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));   // own loads of stage kt landed
   if constexpr (ZERO) {
-    if (kt == last && klast < 32) {
+    if (kt == last && klast < C::BK) {
       asm volatile("" ::: "memory");   // the zeros follow the wait for the loads they overwrite
-      dma_zero_rows<C::NBA>(St, klast, wave, lane);
+      dma_zero_rows<C::NBA, C::BK>(St, klast, wave, lane);
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((C::NSTAGE - 2) * C::PER));
     }
   }
 }
 
-// Step kt on stage Sc; Sp (read in step kt-1) is refilled with step kt+3; Sn
-// holds step kt+1.
-template <class C, bool A_MN, bool B_MN, bool ZERO, class AS, class BS>
+// Sub-step H of stage kt on stage buffer Sc; at H = 0, Sp (read in stage
+// kt-1) is refilled with stage kt+NS-1; Sn holds stage kt+1.
+template <class C, bool A_MN, bool B_MN, bool ZERO, int H, class AS, class BS>
 __device__ __forceinline__ void pp_step(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc, uint16_t* Sp,
                                         uint16_t* Sn, f32x16 (&acc)[C::FM][C::FN], bool hi, int wave, int wm, int wn,
                                         int lane, int klast) {
-  if (!hi) pp_land<C, ZERO>(kt, last, Sc, wave, lane, klast);
-  __builtin_amdgcn_s_barrier();   // lower half: A_kt; upper half: B_kt
-  dma_issue<C>(as, bs, min(kt + C::NSTAGE - 1, last), Sp, wave);
+  if (H == 0 && !hi) pp_land<C, ZERO>(kt, last, Sc, wave, lane, klast);
+  // The reads below stay below this barrier and the previous sub-step's
+  // MFMAs above it (the compiler does not treat s_barrier as a fence).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();   // lower half: A_q; upper half: B_q
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  if (H == 0) dma_issue<C>(as, bs, min(kt + C::NSTAGE - 1, last), Sp, wave);
   DFrags<C> f0, f1;
-  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 0, f0, wm, wn, lane);
-  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 1, f1, wm, wn, lane);
-  if (hi) pp_land<C, ZERO>(kt + 1, last, Sn, wave, lane, klast);
+  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 2 * H, f0, wm, wn, lane);
+  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 2 * H + 1, f1, wm, wn, lane);
+  if (H == C::SUB - 1 && hi) pp_land<C, ZERO>(kt + 1, last, Sn, wave, lane, klast);
   __builtin_amdgcn_sched_barrier(0);   // no MFMA moves above the barrier
-  __builtin_amdgcn_s_barrier();   // lower half: B_kt; upper half: A_kt+1
+  __builtin_amdgcn_s_barrier();   // lower half: B_q; upper half: A_q+1
   __builtin_amdgcn_sched_barrier(0);
   dma_mma<C>(f0, acc);
   dma_mma<C>(f1, acc);
 }
 
+// Every sub-step of stage kt (buffers Sc, Sp, Sn as in pp_step).
+template <class C, bool A_MN, bool B_MN, bool ZERO, class AS, class BS>
+__device__ __forceinline__ void pp_stage(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc, uint16_t* Sp,
+                                         uint16_t* Sn, f32x16 (&acc)[C::FM][C::FN], bool hi, int wave, int wm, int wn,
+                                         int lane, int klast) {
+  pp_step<C, A_MN, B_MN, ZERO, 0>(as, bs, kt, last, Sc, Sp, Sn, acc, hi, wave, wm, wn, lane, klast);
+  if constexpr (C::SUB == 2)
+    pp_step<C, A_MN, B_MN, ZERO, 1>(as, bs, kt, last, Sc, Sp, Sn, acc, hi, wave, wm, wn, lane, klast);
+}
+
+// acc = A . B^T over nk stages of C::BK k; St are the kernel's stage arrays.
+// Ends with every load landed and every wave past its last LDS read.
 template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
 __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, uint16_t* const (&St)[5],
                                             f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn, int lane,
-                                            int klast = 32) {
+                                            int klast = C::BK) {
   static_assert(C::WM == 2, "two row halves of waves");
   constexpr int NS = C::NSTAGE;
 #pragma unroll
@@ -325,15 +366,15 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
   for (; kt + NS <= nk; kt += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u)
-      pp_step<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
-                                   wave, wm, wn, lane, klast);
+      pp_stage<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
+                                    wave, wm, wn, lane, klast);
   }
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
     if (kt + u < nk)
-      pp_step<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
-                                   wave, wm, wn, lane, klast);
-  if (!hi) __builtin_amdgcn_s_barrier();   // the upper half's A_nk
+      pp_stage<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
+                                    wave, wm, wn, lane, klast);
+  if (!hi) __builtin_amdgcn_s_barrier();   // the upper half's last A barrier
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 }
 
@@ -350,11 +391,11 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
   if (jt != (int)(blockIdx.x >> 3)) __syncthreads();
 
 #define DMA_PROLOGUE(C)                                                              \
-  static_assert(C::NSTAGE == 4 || C::NSTAGE == 5, "ring of 4 or 5 stages");         \
+  static_assert(C::NSTAGE >= 2 && C::NSTAGE <= 5, "ring of 2 to 5 stages");           \
   __shared__ __attribute__((aligned(1024))) uint16_t S0[C::STAGE];                  \
   __shared__ __attribute__((aligned(1024))) uint16_t S1[C::STAGE];                  \
-  __shared__ __attribute__((aligned(1024))) uint16_t S2[C::STAGE];                  \
-  __shared__ __attribute__((aligned(1024))) uint16_t S3[C::STAGE];                  \
+  __shared__ __attribute__((aligned(1024))) uint16_t S2[C::NSTAGE > 2 ? C::STAGE : 1]; \
+  __shared__ __attribute__((aligned(1024))) uint16_t S3[C::NSTAGE > 3 ? C::STAGE : 1]; \
   __shared__ __attribute__((aligned(1024))) uint16_t S4[C::NSTAGE > 4 ? C::STAGE : 1]; \
   uint16_t* const St[5] = {S0, S1, S2, S3, S4};                                     \
   const int lane = threadIdx.x & 63;                                                \
@@ -373,8 +414,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
     const uint16_t* X = (const uint16_t*)g.A;
     const int j0 = nt * (C::BN / 2);
     const int* tok = g.tok_of_pos;
-    RowSrc<C::NBA> as;
-    RowSrc<C::NBB> bs;
+    RowSrc<C::NBA, C::BK> as;
+    RowSrc<C::NBB, C::BK> bs;
     // hidden rows of the expert's tokens (byte offsets from X); gate or up
     // rows of the expert's weights (a 16-row load stays in one 32-row group)
     as.init([&](int r, const char*& b, uint32_t& o) {
@@ -388,7 +429,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
       o = (uint32_t)((size_t)g.gu_rs * j * 2);
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, false>(as, bs, H / 32, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, false>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
     epi_gate_up<C, uint16_t, WRITE_A, WRITE_Z>(g, acc, m0, rows, j0, wm, wn, lane);
   }
 }
@@ -403,8 +444,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
     const uint16_t* Aa = (const uint16_t*)g.A;
     const uint16_t* W = (const uint16_t*)g.B + (size_t)e * H * I;
     const int n0 = nt * C::BN;
-    RowSrc<C::NBA> as;
-    RowSrc<C::NBB> bs;
+    RowSrc<C::NBA, C::BK> as;
+    RowSrc<C::NBB, C::BK> bs;
     as.init([&](int r, const char*& b, uint32_t& o) {
       b = (const char*)(Aa + (size_t)m0 * I);
       o = (uint32_t)(min(r, rows - 1) * I * 2);
@@ -414,7 +455,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
       o = (uint32_t)((size_t)min(n0 + r, H - 1) * I * 2);
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, false>(as, bs, I / 32, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, false>(as, bs, I / C::BK, St, acc, wave, wm, wn, lane);
     epi_down<C>(g, acc, m0, rows, n0, wm, wn, lane);
   }
 }
@@ -543,17 +584,21 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
     const uint16_t* dYp = (const uint16_t*)g.A;
     const uint16_t* W = (const uint16_t*)g.B + (size_t)e * H * I;
     const int n0 = nt * C::BN;
-    RowSrc<C::NBA> as;
-    ColSrc<C::NBB> bs;
+    RowSrc<C::NBA, C::BK> as;
+    ColSrc<C::NBB, false, C::BK> bs;
     as.init([&](int r, const char*& b, uint32_t& o) {
       b = (const char*)(dYp + (size_t)m0 * H);
       o = (uint32_t)(min(r, rows - 1) * H * 2);
     }, wave, lane);
     bs.init(W, W, I, H, I, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, true>(as, bs, H / 32, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, true>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
     __syncthreads();   // every wave done with the stages: they hold the epilogue's r values
-    float* const st[4] = {(float*)S0, (float*)S1, (float*)S2, (float*)S3};
+    // four 32 KB regions of the stages: one per stage at BK = 32, two at BK = 64
+    constexpr int RPS = C::STAGE * 2 / 32768;
+    static_assert(RPS * 32768 == C::STAGE * 2 && 4 / RPS <= C::NSTAGE, "four 32 KB regions in the stages");
+    float* const st[4] = {(float*)(St[0 / RPS] + (0 % RPS) * 16384), (float*)(St[1 / RPS] + (1 % RPS) * 16384),
+                          (float*)(St[2 / RPS] + (2 % RPS) * 16384), (float*)(St[3 / RPS] + (3 % RPS) * 16384)};
     dma_epi_down_dgrad<C, 2>(g, acc, m0, rows, n0, nt, wave, wm, wn, lane, st);
   }
 }
@@ -572,8 +617,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
     const int n0 = nt * C::BN;
     const uint16_t* bg = (const uint16_t*)g.gu_g + g.gu_es * e;
     const uint16_t* bu = (const uint16_t*)g.gu_u + g.gu_es * e;
-    RowSrc<C::NBA> as;
-    ColSrc<C::NBB> bs;
+    RowSrc<C::NBA, C::BK> as;
+    ColSrc<C::NBB, false, C::BK> bs;
     as.init([&](int r, const char*& b, uint32_t& o) {
       b = (const char*)(dZ + (size_t)m0 * I2);
       o = (uint32_t)(min(r, rows - 1) * I2 * 2);
@@ -581,7 +626,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
     if (g.gu_sep) bs.init(bg, bu, H, I, H, n0, wave, lane);
     else bs.init(bg, bg, H, I2, H, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, true>(as, bs, I2 / 32, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, true>(as, bs, I2 / C::BK, St, acc, wave, wm, wn, lane);
     epi_gate_up_dgrad<C>(g, acc, m0, rows, n0, wm, wn, lane);
   }
 }
@@ -632,13 +677,13 @@ __global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     const uint16_t* Ae = Ag + (size_t)off * M;
     const uint16_t* Be = Bg + (size_t)off * N;
-    ColSrc<C::NBA, true> as;
-    ColSrc<C::NBB, true> bs;
+    ColSrc<C::NBA, true, C::BK> as;
+    ColSrc<C::NBB, true, C::BK> bs;
     as.init(Ae, Ae, M, 0, M, m0, wave, lane, cnt - 1);
     bs.init(Be, Be, N, 0, N, n0, wave, lane, cnt - 1);
-    const int nk = (cnt + 31) >> 5;
+    const int nk = (cnt + C::BK - 1) / C::BK;
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, true, true, true>(as, bs, nk, St, acc, wave, wm, wn, lane, cnt - (nk - 1) * 32);
+    pp_mainloop<C, true, true, true>(as, bs, nk, St, acc, wave, wm, wn, lane, cnt - (nk - 1) * C::BK);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
@@ -689,9 +734,14 @@ bool dma_enabled(const GemmProblem& pb) {
 constexpr int kLargeTileMinSlots = 512;
 int large_tile_min_slots(const GemmProblem& pb) { return dma_enabled(pb) ? kLargeTileMinSlots : 0x7fffffff; }
 
-hipError_t dma_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
-                       hipStream_t s) {
-  using C = DCfgB;
+// 64-k stages (whole cache lines per k-contiguous load) when every k
+// dimension of the token-row products (H, I, and I as the split point of
+// separate gate / up tensors) is a multiple of 64; 32-k stages otherwise.
+static bool dma_bk64(const GemmProblem& pb) { return pb.H % 64 == 0 && pb.I % 64 == 0; }
+
+template <class C>
+static hipError_t dma_gate_up_impl(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
+                                   hipStream_t s) {
   GemmProblem p = pb;
   p.tile_set = 1;
   GArgs g = base_args(p, C::BM);
@@ -707,8 +757,14 @@ hipError_t dma_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, vo
   });
 }
 
-hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
-  using C = DCfgB;
+hipError_t dma_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
+                       hipStream_t s) {
+  return dma_bk64(pb) ? dma_gate_up_impl<DCfgB64>(pb, X, Wgu, a_out, z_out, s)
+                      : dma_gate_up_impl<DCfgB>(pb, X, Wgu, a_out, z_out, s);
+}
+
+template <class C>
+static hipError_t dma_down_impl(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
   GemmProblem p = pb;
   p.tile_set = 1;
   GArgs g = base_args(p, C::BM);
@@ -718,9 +774,13 @@ hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* 
   return run_kernel("down_weighted_big", s, [&] { dma_down_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
-hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
-                          float* partials, int nparts, hipStream_t s) {
-  using C = DCfgB;
+hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
+  return dma_bk64(pb) ? dma_down_impl<DCfgB64>(pb, a, Wd, Yp, s) : dma_down_impl<DCfgB>(pb, a, Wd, Yp, s);
+}
+
+template <class C>
+static hipError_t dma_down_dgrad_impl(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ,
+                                      void* aw, float* partials, int nparts, hipStream_t s) {
   GemmProblem p = pb;
   p.tile_set = 1;
   GArgs g = base_args(p, C::BM);
@@ -731,8 +791,15 @@ hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd,
   return run_kernel("down_dgrad_glu_bwd_big", s, [&] { dma_down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
-hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
-  using C = DCfgB;
+hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
+                          float* partials, int nparts, hipStream_t s) {
+  return dma_bk64(pb) ? dma_down_dgrad_impl<DCfgB64>(pb, dY, Wd, Z, dZ, aw, partials, nparts, s)
+                      : dma_down_dgrad_impl<DCfgB>(pb, dY, Wd, Z, dZ, aw, partials, nparts, s);
+}
+
+template <class C>
+static hipError_t dma_gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp,
+                                         hipStream_t s) {
   GemmProblem p = pb;
   p.tile_set = 1;
   GArgs g = base_args(p, C::BM);
@@ -741,6 +808,11 @@ hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* 
   g.ntn = (pb.H + C::BN - 1) / C::BN;
   const long grid = persistent_grid();
   return run_kernel("gate_up_dgrad_big", s, [&] { dma_gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+}
+
+hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
+  return dma_bk64(pb) ? dma_gate_up_dgrad_impl<DCfgB64>(pb, dZ, Wgu, dXp, s)
+                      : dma_gate_up_dgrad_impl<DCfgB>(pb, dZ, Wgu, dXp, s);
 }
 
 // Weight gradients of the experts with more than hot_min positions; every

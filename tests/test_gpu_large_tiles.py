@@ -42,6 +42,20 @@ def test_large_tile_experts_match_oracle(act, layout, save):
     run_and_compare(large_tile_inputs(act, layout, 51), save=save, grad_dtype="bf16", poison=True)
 
 
+@pytest.mark.parametrize("act,layout", [("clamped", "interleaved"), ("swiglu", "concat")])
+def test_large_tile_experts_64k_stages(act, layout):
+    """H = 320 and I = 192 (multiples of 64): the token-row kernels take
+    stages of 64 k (gate_up 5 stages, an odd count for the two-stage ring;
+    down 3).  N stays ragged: gate_up 384 dZ columns (128 of 256 in the
+    second tile), down 320 (64), the input gradients 320 and 192."""
+    E, K = len(COUNTS), 1
+    T = sum(COUNTS)
+    rng = np.random.default_rng(59)
+    ids = rng.permutation(np.repeat(np.arange(E), COUNTS)).reshape(T, K).astype(np.int32)
+    inp = small_inputs(T, 320, 192, E, K, "bf16", act, layout, seed=59, ids=ids)
+    run_and_compare(inp, save=act == "clamped", grad_dtype="bf16", poison=True)
+
+
 @pytest.mark.parametrize("layout", ["interleaved", "concat"])
 def test_large_tile_separate_weights(layout):
     check_separate(large_tile_inputs("swiglu", layout, 53), "swiglu", layout, "bf16", "fp32", True)
