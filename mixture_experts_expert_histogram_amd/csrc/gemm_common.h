@@ -3,6 +3,7 @@
 // arguments, token-row tile mapping and the fused epilogues of the
 // token-row GEMMs (used by both GEMM engines).
 #pragma once
+#include <cstddef>
 #include "moe_internal.h"
 
 namespace moe {
@@ -112,6 +113,13 @@ struct GArgs {
   long gu_es, gu_rs;
   int gu_sep;   // separate gate and up tensors (Z and dZ columns then concatenated)
 };
+// GArgs is passed by value as the kernel argument: the host and device passes
+// of every source file must lay it out alike (no LDS pointers, which are
+// 4 bytes on the device, and 8-byte pointers and longs on both sides).
+static_assert(sizeof(void*) == 8 && sizeof(long) == 8, "64-bit pointers and longs on host and device");
+static_assert(sizeof(GArgs) == 208 && offsetof(GArgs, T) == 88 && offsetof(GArgs, hot_min) == 148 &&
+                  offsetof(GArgs, gu_g) == 152 && offsetof(GArgs, gu_es) == 184 && offsetof(GArgs, gu_sep) == 200,
+              "kernel-argument layout");
 
 // Row j of expert e's gate (up = 0) or up (up = 1) projection.
 template <typename P>

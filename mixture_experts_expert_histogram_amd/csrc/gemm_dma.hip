@@ -341,7 +341,11 @@ __device__ __forceinline__ void pp_stage(const AS& as, const BS& bs, int kt, int
 }
 
 // acc = A . B^T over nk stages of C::BK k; St are the kernel's stage arrays.
-// Ends with every load landed and every wave past its last LDS read.
+// Ends with every wave past its last LDS read and the wave's own loads
+// landed.  The last NS - 1 stages still refill stages (with the last stage's
+// data, so that the wait counts stay constant): another wave's refill can
+// land in a stage after this wave returns, so a workgroup barrier must
+// follow before the stages are written for anything else.
 template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
 __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, uint16_t* const (&St)[5],
                                             f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn, int lane,
@@ -381,14 +385,15 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
 // Persistent workgroups, one per CU: workgroup b walks tiles b / 8,
 // b / 8 + gridDim / 8, ... of XCD b % 8's contiguous range of the tile table
 // (TILE_LOOP).  The barrier between tiles keeps a tile's first loads out of
-// stages that slower waves may still be reading for the previous one.
+// stages that slower waves may still be reading for the previous one (its
+// epilogue included); every wave's own loads have landed before it.
 #define TILE_LOOP(C)                                                                          \
   int e, m0, rows, nt;                                                                        \
   for (int jt = blockIdx.x >> 3; row_tile_at<C::BM>(g, blockIdx.x & 7, jt, e, m0, rows, nt); \
        jt += gridDim.x >> 3)
 
 #define TILE_SYNC()                                        \
-  if (jt != (int)(blockIdx.x >> 3)) __syncthreads();
+  if (jt != (int)(blockIdx.x >> 3)) lds_barrier();
 
 #define DMA_PROLOGUE(C)                                                              \
   static_assert(C::NSTAGE >= 2 && C::NSTAGE <= 5, "ring of 2 to 5 stages");           \
@@ -401,6 +406,94 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
   const int lane = threadIdx.x & 63;                                                \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);                \
   const int wm = wave / C::WN, wn = wave % C::WN;
+
+// ---------------------------------------------------------------- epilogues through LDS
+// After the mainloop the stages are free (every wave is past its last read):
+// the epilogues put the tile's 256 x 256 fp32 results into them in two halves
+// of 128 rows (the waves of row half h write theirs: fragment fm into 32 KB
+// region fm, 32 rows x 256 columns, 16-byte chunks XORed with row % 16), then
+// each wave takes rows 8q + wave of the half (q = 0..15), so that every
+// global access moves whole row segments: a store of 64 lanes x 16 bytes
+// writes 1 KB of one row (8 cache lines), where the accumulator layout
+// spreads a store over 32 rows.  Between the halves and the tiles a barrier
+// waits only for LDS (lds_barrier): the previous rows' global stores stay in
+// flight.
+
+// A workgroup barrier that orders LDS accesses only (global stores in flight
+// stay in flight; __syncthreads would wait for them).  The asm statements
+// keep the compiler's memory accesses on their side of it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Float index of chunk `chunk` (4 floats) of row `row` of a 32-row region.
+__device__ __forceinline__ int epi_chunk(int row, int chunk) { return (row << 8) + ((chunk ^ (row & 15)) << 2); }
+
+template <class C>
+__device__ __forceinline__ void epi_r_to_lds(f32x16 (&acc)[C::FM][C::FN], float* const (&st)[4], int wn, int lane) {
+  static_assert(C::FM == 4 && C::BN == 256, "fragment fm of a 128-row half fills region fm");
+  const int row = lane & 31;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int chunk = (wn * C::WTN + fn * 32 + acc_col4(vg, lane)) >> 2;
+        *(float4*)(st[fm] + epi_chunk(row, chunk)) =
+            make_float4(acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
+      }
+}
+
+// The four 32 KB regions of the stages: one per stage at BK = 32, two at 64.
+template <class C>
+__device__ __forceinline__ void epi_regions(uint16_t* const (&St)[5], float* (&st)[4]) {
+  constexpr int RPS = C::STAGE * 2 / 32768;
+  static_assert(RPS * 32768 == C::STAGE * 2 && 4 / RPS <= C::NSTAGE, "four 32 KB regions in the stages");
+#pragma unroll
+  for (int q = 0; q < 4; ++q) st[q] = (float*)(St[q / RPS] + (q % RPS) * 16384);
+}
+
+// Routing weights of the tile rows a wave takes in dma_epi_rows, one per lane
+// (lane 16 h + q: row 128 h + 8 q + wave), loaded before any epilogue store:
+// a load issued after the stores would wait for all of them (vector memory
+// counts complete in order).  epi_row_weight reads row tr's back.
+__device__ __forceinline__ float epi_row_weights(const float* w_of_pos, int m0, int rows, int wave, int lane) {
+  const int tr = ((lane >> 4) & 1) * 128 + (lane & 15) * 8 + wave;
+  return w_of_pos[m0 + min(tr, rows - 1)];
+}
+__device__ __forceinline__ float epi_row_weight(float wl, int tr) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl),
+                                                             ((tr >> 7) << 4) + ((tr & 127) >> 3)));
+}
+
+// The tile through LDS: row(tr, lr, r) for every tile row tr < rows, with lr
+// the row's LDS floats (chunk c at lr + ((c ^ r) << 2), r = tr % 16), called
+// by wave tr % 8.
+template <class C, class RowFn>
+__device__ __forceinline__ void dma_epi_rows(f32x16 (&acc)[C::FM][C::FN], int rows, int wave, int wm, int wn,
+                                             int lane, float* const (&st)[4], RowFn row) {
+  static_assert(C::NW == 8 && C::WM == 2, "8 waves over rows 8q + wave of a 128-row half");
+  lds_barrier();   // every wave's loads into the stages have landed (see pp_mainloop)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) epi_r_to_lds<C>(acc, st, wn, lane);
+    lds_barrier();
+    const int hrows = rows - h * 128;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const float* reg = st[qq];
+#pragma unroll 2
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int hr = (qq * 4 + q4) * 8 + wave;
+        if (hr < hrows) row(h * 128 + hr, reg + ((hr & 31) << 8), hr & 15);
+      }
+    }
+    if (h == 0) lds_barrier();   // half 0 read before half 1 overwrites it
+  }
+}
 
 // ---------------------------------------------------------------- gate_up fwd
 // B rows: 32-row groups alternate gate and up rows of the same 32 activation
@@ -430,7 +523,33 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
     pp_mainloop<C, false, false>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
-    epi_gate_up<C, uint16_t, WRITE_A, WRITE_Z>(g, acc, m0, rows, j0, wm, wn, lane);
+    float* st[4];
+    epi_regions<C>(St, st);
+    // lane l: activation columns j0 + 2l, 2l + 1, i.e. tile columns c, c + 1
+    // (gate) and c + 32, c + 33 (up) with c = 64 (l / 16) + 2 (l % 16)
+    const int j = j0 + 2 * lane;
+    const int c = ((lane >> 4) << 6) + ((lane & 15) << 1);
+    const bool col_ok = j < I;   // I is even, so j + 1 < I too
+    uint16_t* a_out = (uint16_t*)g.out0;
+    float* z_out = (float*)g.out1;
+    dma_epi_rows<C>(acc, rows, wave, wm, wn, lane, st, [&](int tr, const float* lr, int r) {
+      const float2 gv = *(const float2*)(lr + (((c >> 2) ^ r) << 2) + (c & 3));
+      const float2 uv = *(const float2*)(lr + ((((c + 32) >> 2) ^ r) << 2) + (c & 3));
+      if (!col_ok) return;
+      const size_t p = (size_t)(m0 + tr);
+      if (WRITE_A)
+        *(uint32_t*)(a_out + p * I + j) = pack_bf16(glu_fwd(gv.x, uv.x, g.act, g.limit, g.alpha),
+                                                    glu_fwd(gv.y, uv.y, g.act, g.limit, g.alpha));
+      if (WRITE_Z) {
+        float* zr = z_out + p * 2 * I;
+        if (g.layout) {
+          *(float4*)(zr + 2 * j) = make_float4(gv.x, uv.x, gv.y, uv.y);
+        } else {
+          *(float2*)(zr + j) = gv;
+          *(float2*)(zr + I + j) = uv;
+        }
+      }
+    });
   }
 }
 
@@ -456,36 +575,25 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
     pp_mainloop<C, false, false>(as, bs, I / C::BK, St, acc, wave, wm, wn, lane);
-    epi_down<C>(g, acc, m0, rows, n0, wm, wn, lane);
+    float* st[4];
+    epi_regions<C>(St, st);
+    // Y fp32 [S,H] = routing weight * (a . Wd^T); lane l: columns n0 + 4l .. +3
+    const int n = n0 + 4 * lane;
+    float* Y = (float*)g.out0;
+    const float wl = epi_row_weights(g.w_of_pos, m0, rows, wave, lane);
+    dma_epi_rows<C>(acc, rows, wave, wm, wn, lane, st, [&](int tr, const float* lr, int r) {
+      const float4 v = *(const float4*)(lr + ((lane ^ r) << 2));
+      const float w = epi_row_weight(wl, tr);
+      if (n < H) *(float4*)(Y + (size_t)(m0 + tr) * H + n) = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+    });
   }
 }
 
 // ---------------------------------------------------------------- down dgrad
-// The epilogue goes through LDS, so that its Z reads and dZ / aw stores move
-// whole rows.  The tile's r values go to the four stages in two halves of 128
-// rows (the waves of row half h write theirs: fragment fm into stage fm, 32
-// rows x 256 fp32 columns, 16-byte chunks XORed with row % 16), then each wave
-// takes rows 8q + wave of the half, lane l columns 4l .. 4l + 3: one
-// contiguous 2 KB (Z), 1 KB (dZ) and 512 B (aw) access per row and wave, in
-// batches of 2 rows with the next batch's Z loads in flight.  Written from
-// the accumulators, every lane of a wave hit 32 rows.
-__device__ __forceinline__ int epi_chunk(int row, int chunk) { return (row << 8) + ((chunk ^ (row & 15)) << 2); }
-
-template <class C>
-__device__ __forceinline__ void epi_r_to_lds(f32x16 (&acc)[C::FM][C::FN], float* const (&st)[4], int wn, int lane) {
-  static_assert(C::FM == 4 && C::BN == 256, "fragment fm of a 128-row half fills stage fm");
-  const int row = lane & 31;
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int chunk = (wn * C::WTN + fn * 32 + acc_col4(vg, lane)) >> 2;
-        *(float4*)(st[fm] + epi_chunk(row, chunk)) =
-            make_float4(acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
-      }
-}
+// The epilogue goes through LDS (as above) with its own row loop: lane l
+// takes columns 4l .. 4l + 3 of a row, so Z (2 KB), dZ (1 KB) and aw (512 B)
+// move as one contiguous access per row and wave, in batches of 2 rows with
+// the next batch's Z loads in flight.
 
 // Z of one row at columns ic .. ic + 3 (interleaved: g, u pairs over 8 floats;
 // concatenated: gate, then up at + I).
@@ -507,10 +615,12 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
   const bool col_ok = i < I;
   const int ic = col_ok ? i : I - 4;   // I is a multiple of 4
   const int slot = nt * 2 + (lane >> 5);   // 128-column partial slot of this lane's columns
+  const float wl = epi_row_weights(g.w_of_pos, m0, rows, wave, lane);
+  lds_barrier();   // every wave's loads into the stages have landed (see pp_mainloop)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (wm == h) epi_r_to_lds<C>(acc, st, wn, lane);
-    __syncthreads();
+    lds_barrier();
     const int hrows = rows - h * 128;   // valid rows of this half (may be <= 0)
     if (hrows > 0) {
       float4 za[2][RB], zb[2][RB];
@@ -525,7 +635,7 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
         for (int r = 0; r < RB; ++r) {
           const int q = b * RB + r, hr = q * 8 + wave;
           const size_t p = (size_t)pos(q);
-          const float w = g.w_of_pos[p];
+          const float w = epi_row_weight(wl, h * 128 + hr);
           const float4 rv = *(const float4*)(st[q >> 2] + epi_chunk(hr & 31, lane));
           const float4 z0 = za[buf][r], z1 = zb[buf][r];
           float gv[4], uv[4];
@@ -570,7 +680,7 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
         process(b, b & 1);
       }
     }
-    if (h == 0) __syncthreads();   // half 0 read before half 1 overwrites it
+    if (h == 0) lds_barrier();   // half 0 read before half 1 overwrites it
   }
 }
 
@@ -593,12 +703,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
     bs.init(W, W, I, H, I, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
     pp_mainloop<C, false, true>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
-    __syncthreads();   // every wave done with the stages: they hold the epilogue's r values
-    // four 32 KB regions of the stages: one per stage at BK = 32, two at BK = 64
-    constexpr int RPS = C::STAGE * 2 / 32768;
-    static_assert(RPS * 32768 == C::STAGE * 2 && 4 / RPS <= C::NSTAGE, "four 32 KB regions in the stages");
-    float* const st[4] = {(float*)(St[0 / RPS] + (0 % RPS) * 16384), (float*)(St[1 / RPS] + (1 % RPS) * 16384),
-                          (float*)(St[2 / RPS] + (2 % RPS) * 16384), (float*)(St[3 / RPS] + (3 % RPS) * 16384)};
+    float* st[4];
+    epi_regions<C>(St, st);
     dma_epi_down_dgrad<C, 2>(g, acc, m0, rows, n0, nt, wave, wm, wn, lane, st);
   }
 }
@@ -627,7 +733,15 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
     else bs.init(bg, bg, H, I2, H, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
     pp_mainloop<C, false, true>(as, bs, I2 / C::BK, St, acc, wave, wm, wn, lane);
-    epi_gate_up_dgrad<C>(g, acc, m0, rows, n0, wm, wn, lane);
+    float* st[4];
+    epi_regions<C>(St, st);
+    // dXp fp32 [S,H]; lane l: columns n0 + 4l .. +3
+    const int n = n0 + 4 * lane;
+    float* dXp = (float*)g.out0;
+    dma_epi_rows<C>(acc, rows, wave, wm, wn, lane, st, [&](int tr, const float* lr, int r) {
+      const float4 v = *(const float4*)(lr + ((lane ^ r) << 2));
+      if (n < H) *(float4*)(dXp + (size_t)(m0 + tr) * H + n) = v;
+    });
   }
 }
 
@@ -666,7 +780,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
   for (int j = blockIdx.x >> 3;; j += gridDim.x >> 3) {
     const int t = dealt_tile<32>(j, total);
     if (t < 0) break;
-    if (j != (int)(blockIdx.x >> 3)) __syncthreads();   // the previous tile's stage reads are done
+    if (j != (int)(blockIdx.x >> 3)) lds_barrier();   // the previous tile's stage reads are done
     const int er = t / per_e, local = t - er * per_e;
     const int e = g.expert_order[er];
     const int off = g.offsets[e], cnt = g.offsets[e + 1] - off;   // cnt > hot_min > 0
