@@ -104,7 +104,7 @@ def measured_traffic(kernel, workload, grad_dtype):
 
 # ------------------------------------------------------------------ per-kernel model
 RES_KMAX = 240   # the resident-operand weight gradient's limit (positions per expert)
-LONG_MIN = 512  # experts with more positions take the long-K weight gradient
+LONG_MIN = 512  # experts with more positions take the long-K weight gradient (without the large-tile engine)
 LARGE_MIN = 512  # experts with at least this many slots take the 256-row token-row tiles
 
 
@@ -122,6 +122,14 @@ def large_tile_experts(wl, counts):
     rows_big = (counts + 255) // 256 * 256
     rows_small = (counts + bms - 1) // bms * bms
     return (counts >= LARGE_MIN) | ((counts > 0) & (rows_big <= rows_small))
+
+
+def large_wgrad(wl):
+    """Whether the weight gradients of experts above RES_KMAX positions run on
+    the large-tile engine (its token-row conditions, and every position row of
+    dZ and the hidden states below 2^31 bytes)."""
+    lim = 1 << 31
+    return large_tiles(wl) and wl.S * 4 * wl.I < lim and wl.S * 2 * wl.H < lim
 
 
 def large_tiles(wl):
@@ -174,8 +182,9 @@ def kernel_model(wl, counts, grad_bytes):
         rows(big, "_big")
     # Weight gradients.  With bf16 operands, experts with at most RES_KMAX
     # positions (and those without any) take the resident-operand kernel,
-    # named wgrad_down / wgrad_gate_up, those with more than LONG_MIN the
-    # long-K kernel (*_long) and the rest the tiled kernel (*_hot); with fp32
+    # named wgrad_down / wgrad_gate_up; the rest take the large-tile kernel
+    # (*_long) where that engine applies, else those with more than LONG_MIN
+    # the long-K kernel (*_long) and the others the tiled one (*_hot); with fp32
     # operands the tiled kernel takes every expert under the plain names.
     # Each writes its experts' gradients; the hidden / output-gradient rows it
     # reads are prorated by the positions it covers.
@@ -188,7 +197,7 @@ def kernel_model(wl, counts, grad_bytes):
         return down, gu
     if wl.dtype == "bf16":
         small = counts <= RES_KMAX
-        long_ = counts > LONG_MIN
+        long_ = counts > (RES_KMAX if large_wgrad(wl) else LONG_MIN)
         mid = ~small & ~long_
         m["wgrad_down"], m["wgrad_gate_up"] = wgrad(small)
         if mid.any():

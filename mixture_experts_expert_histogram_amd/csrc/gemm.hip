@@ -1718,10 +1718,13 @@ static hipError_t wgrad_res_impl(const GemmProblem& pb, const void* A, const voi
   });
 }
 
-// Experts with more than kLongMin positions take the long-K kernel (Zipf
-// batch weight gradients: 8.87 ms at 512, 8.95 at 384, 9.16 at 1024; at 256
-// the backward workload's 257-296-position experts were slower than on the
-// tiled kernel, 7.34 against 6.15 ms).
+// Experts with more than kLongMin positions take the register-staged long-K
+// kernel (Zipf batch weight gradients: 8.87 ms at 512, 8.95 at 384, 9.16 at
+// 1024; at 256 the backward workload's 257-296-position experts were slower
+// than on the tiled kernel, 7.34 against 6.15 ms).  Where the large-tile
+// engine applies, it takes every expert above kResKmax instead (backward
+// workload: 4.89 ms against 5.95 on the tiled kernel for its 241-512-position
+// experts; Zipf batch: 6.40 against 6.69 ms for all experts above 240).
 constexpr int kLongMin = 512;
 
 template <bool GU, typename OutT>
@@ -1745,14 +1748,16 @@ template <bool GU>
 static hipError_t wgrad_dispatch(const GemmProblem& pb, const void* A, const void* B, void* dW, hipStream_t s) {
   if (pb.dtype == 0 && pb.S > 0) {
     // bf16 operands: experts with at most kResKmax positions (and those
-    // without any) on the resident-operand kernel, then the rest
+    // without any) on the resident-operand kernel, then the rest: all on the
+    // large-tile kernel where it applies, else up to kLongMin on the tiled
+    // kernel and above on the long-K one
     const hipError_t e = pb.gdtype == 0 ? wgrad_res_impl<GU, uint16_t>(pb, A, B, dW, s)
                                         : wgrad_res_impl<GU, float>(pb, A, B, dW, s);
     if (e != hipSuccess) return e;
+    if (dma_wgrad_enabled(pb)) return dma_wgrad(pb, GU, A, B, dW, kResKmax, s);
     const hipError_t e2 = pb.gdtype == 0 ? wgrad_impl<CfgWB256, GU, uint16_t>(pb, A, B, dW, s, kResKmax, kLongMin)
                                          : wgrad_impl<CfgWB, GU, float>(pb, A, B, dW, s, kResKmax, kLongMin);
     if (e2 != hipSuccess) return e2;
-    if (dma_wgrad_enabled(pb)) return dma_wgrad(pb, GU, A, B, dW, kLongMin, s);
     return pb.gdtype == 0 ? wgrad_long_impl<GU, uint16_t>(pb, A, B, dW, s)
                           : wgrad_long_impl<GU, float>(pb, A, B, dW, s);
   }

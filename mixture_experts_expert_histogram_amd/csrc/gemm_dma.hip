@@ -419,6 +419,17 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
 // waits only for LDS (lds_barrier): the previous rows' global stores stay in
 // flight.
 
+// Non-temporal stores of 4 values (8 bytes bf16, 16 bytes fp32).
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+template <typename T> __device__ __forceinline__ void store4_nt(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4_nt<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(u32x2_nt{pack_bf16(a, b), pack_bf16(c, d)}, (u32x2_nt*)p);
+}
+template <> __device__ __forceinline__ void store4_nt<float>(float* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(f32x4_nt{a, b, c, d}, (f32x4_nt*)p);
+}
+
 // A workgroup barrier that orders LDS accesses only (global stores in flight
 // stay in flight; __syncthreads would wait for them).  The asm statements
 // keep the compiler's memory accesses on their side of it.
@@ -798,10 +809,14 @@ __global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
     const int nk = (cnt + C::BK - 1) / C::BK;
     f32x16 acc[C::FM][C::FN];
     pp_mainloop<C, true, true, true>(as, bs, nk, St, acc, wave, wm, wn, lane, cnt - (nk - 1) * C::BK);
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int m = m0 + wm * C::WTM + fm * 32 + (lane & 31);
-      if (m >= M) continue;
+    float* st[4];
+    epi_regions<C>(St, st);
+    // through LDS, whole row segments (512 bytes bf16, 1 KB fp32), written
+    // once and not read again here (non-temporal); lane l: columns n0 + 4l .. +3
+    const int n = n0 + 4 * lane;
+    dma_epi_rows<C>(acc, min(M - m0, C::BM), wave, wm, wn, lane, st, [&](int tr, const float* lr, int r) {
+      const float4 v = *(const float4*)(lr + ((lane ^ r) << 2));
+      const int m = m0 + tr;
       OutT* row;
       if (GATE_UP && g.gu_sep) {   // separate dW_gate, dW_up: row m is a dZ column
         int up, jj;
@@ -810,16 +825,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
       } else {
         row = dW + ((size_t)e * M + m) * N;
       }
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int vg = 0; vg < 4; ++vg) {
-          const int n = n0 + wn * C::WTN + fn * 32 + acc_col4(vg, lane);
-          if (n < N)
-            store4<OutT>(row + n, acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2],
-                         acc[fm][fn][vg * 4 + 3]);
-        }
-    }
+      if (n < N) store4_nt<OutT>(row + n, v.x, v.y, v.z, v.w);
+    });
   }
 }
 

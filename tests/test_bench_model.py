@@ -1,11 +1,13 @@
 """The benchmark's roofline model of one launch per kernel (host logic, CPU).
 
-With bf16 operands the weight gradients run as three kernels: the
-resident-operand one for experts of at most RES_KMAX positions (and empty
-experts), the long-K one for experts of more than LONG_MIN and the tiled one
-for the rest, whether the gradients are stored in bf16 or fp32.  The model
-entries must split the useful flops and the gradient bytes by expert
-exactly; with fp32 operands a single entry covers every expert.
+With bf16 operands the weight gradients run as the resident-operand kernel
+for experts of at most RES_KMAX positions (and empty experts) and the
+large-tile kernel for the rest where that engine applies (H and I multiples
+of 32), else as three kernels: the resident one, the long-K one for experts
+of more than LONG_MIN and the tiled one for the rest, whether the gradients
+are stored in bf16 or fp32.  The model entries must split the useful flops
+and the gradient bytes by expert exactly; with fp32 operands a single entry
+covers every expert.
 """
 import numpy as np
 import pytest
@@ -15,27 +17,31 @@ from synth import WORKLOADS, Workload
 
 
 @pytest.mark.parametrize("grad_bytes", [2, 4])
-def test_weight_gradient_split_covers_every_expert(grad_bytes):
+@pytest.mark.parametrize("I,large", [(2880, True), (2872, False)])
+def test_weight_gradient_split_covers_every_expert(grad_bytes, I, large):
     E = 128
     counts = np.zeros(E, dtype=np.int64)
     rng = np.random.default_rng(0)
     counts[:100] = rng.integers(1, bench.RES_KMAX + 1, size=100)
     counts[100:120] = rng.integers(bench.RES_KMAX + 1, 4000, size=20)
     counts[120] = bench.RES_KMAX            # at the limit: resident
-    counts[121] = bench.RES_KMAX + 1        # just above: tiled
-    counts[122] = bench.LONG_MIN            # at the limit: tiled
-    counts[123] = bench.LONG_MIN + 1        # just above: long-K
+    counts[121] = bench.RES_KMAX + 1        # just above: tiled (large-tile where it applies)
+    counts[122] = bench.LONG_MIN            # at the limit: tiled (large-tile)
+    counts[123] = bench.LONG_MIN + 1        # just above: long-K (large-tile)
     # experts 124.. are empty; one slot per token so that S = T = counts.sum()
-    wl = Workload("model", int(counts.sum()), 2880, 2880, E, 1, "bf16", "clamped", "interleaved")
+    wl = Workload("model", int(counts.sum()), 2880, I, E, 1, "bf16", "clamped", "interleaved")
+    assert bench.large_wgrad(wl) == large
     m = bench.kernel_model(wl, counts, grad_bytes)
-    H, I, S = wl.H, wl.I, wl.S
+    H, S = wl.H, wl.S
     for name, per_flop in [("wgrad_down", 2.0), ("wgrad_gate_up", 4.0)]:
         parts = [m[name]] + [m[name + suf] for suf in ("_hot", "_long") if name + suf in m]
-        assert len(parts) == 3
+        assert len(parts) == (2 if large else 3)
         assert sum(p[1] for p in parts) == pytest.approx(per_flop * S * H * I)
-        small, long_ = counts <= bench.RES_KMAX, counts > bench.LONG_MIN
+        small = counts <= bench.RES_KMAX
+        long_ = counts > (bench.RES_KMAX if large else bench.LONG_MIN)
         assert m[name][1] == pytest.approx(per_flop * counts[small].sum() * H * I)
-        assert m[name + "_hot"][1] == pytest.approx(per_flop * counts[~small & ~long_].sum() * H * I)
+        if not large:
+            assert m[name + "_hot"][1] == pytest.approx(per_flop * counts[~small & ~long_].sum() * H * I)
         assert m[name + "_long"][1] == pytest.approx(per_flop * counts[long_].sum() * H * I)
         # every expert's gradient is written once, by exactly one of the kernels,
         # and the hidden / output-gradient rows are read once in total; the

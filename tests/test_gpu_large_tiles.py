@@ -94,6 +94,20 @@ def test_large_tile_weight_grads(grad_dtype):
     run_and_compare(weight_grad_inputs("interleaved", 61), save=True, grad_dtype=grad_dtype, poison=True)
 
 
+@pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
+def test_large_tile_weight_grads_short_k(grad_dtype):
+    """Experts of 241, 300, 464, 465 and 700 positions (the large-tile
+    weight gradient: 8 to 22 steps of 32, ragged last steps of 1 to 28) and
+    240 (the resident-operand kernel) at H = 544, I = 1056."""
+    counts = [700, 465, 464, 300, 241, 240]
+    E, K = len(counts), 1
+    T = sum(counts)
+    rng = np.random.default_rng(67)
+    ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
+    inp = small_inputs(T, 544, 1056, E, K, "bf16", "swiglu", "interleaved", seed=67, ids=ids)
+    run_and_compare(inp, save=True, grad_dtype=grad_dtype, poison=True)
+
+
 @pytest.mark.parametrize("layout", ["interleaved", "concat"])
 def test_large_tile_weight_grads_separate(layout):
     """Separate gate and up gradient tensors: a 256-row tile of dZ columns
