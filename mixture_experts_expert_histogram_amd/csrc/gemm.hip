@@ -1563,8 +1563,9 @@ hipError_t launch_gate_up(const GemmProblem& pb, const void* X, const void* Wgu,
     const hipError_t e = dma_gate_up(pb, X, Wgu, a_out, z_out, s);
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
-    return use_bm192(pb) ? gate_up_dispatch<CfgB192>(ps, X, Wgu, a_out, z_out, s)
-                         : gate_up_dispatch<CfgBW>(ps, X, Wgu, a_out, z_out, s);
+    if (use_bm192(pb)) return gate_up_dispatch<CfgB192>(ps, X, Wgu, a_out, z_out, s);
+    return dma_small_enabled(pb) ? dma_gate_up_small(ps, X, Wgu, a_out, z_out, s)
+                                 : gate_up_dispatch<CfgBW>(ps, X, Wgu, a_out, z_out, s);
   }
   if (use_bm256(pb)) return gate_up_dispatch<CfgB256>(pb, X, Wgu, a_out, z_out, s);
   return use_bm192(pb) ? gate_up_dispatch<CfgB192>(pb, X, Wgu, a_out, z_out, s)
@@ -1587,7 +1588,8 @@ hipError_t launch_down(const GemmProblem& pb, const void* a, const void* Wd, voi
     const hipError_t e = dma_down(pb, a, Wd, Yp, s);
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
-    return use_bm192(pb) ? down_impl<CfgB192>(ps, a, Wd, Yp, s) : down_impl<CfgBW>(ps, a, Wd, Yp, s);
+    if (use_bm192(pb)) return down_impl<CfgB192>(ps, a, Wd, Yp, s);
+    return dma_small_enabled(pb) ? dma_down_small(ps, a, Wd, Yp, s) : down_impl<CfgBW>(ps, a, Wd, Yp, s);
   }
   if (use_bm256(pb)) return down_impl<CfgB256>(pb, a, Wd, Yp, s);
   return use_bm192(pb) ? down_impl<CfgB192>(pb, a, Wd, Yp, s) : down_impl<CfgB>(pb, a, Wd, Yp, s);
@@ -1620,8 +1622,9 @@ hipError_t launch_down_dgrad(const GemmProblem& pb, const void* dY, const void* 
     const hipError_t e = dma_down_dgrad(pb, dY, Wd, Z, dZ, aw, partials, *nparts, s);
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
-    return use_bm192(pb) ? down_dgrad_impl<CfgB192>(ps, dY, Wd, Z, dZ, aw, partials, s)
-                         : down_dgrad_impl<CfgBW>(ps, dY, Wd, Z, dZ, aw, partials, s);
+    if (use_bm192(pb)) return down_dgrad_impl<CfgB192>(ps, dY, Wd, Z, dZ, aw, partials, s);
+    return dma_small_enabled(pb) ? dma_down_dgrad_small(ps, dY, Wd, Z, dZ, aw, partials, down_dgrad_nparts(pb.I), s)
+                                 : down_dgrad_impl<CfgBW>(ps, dY, Wd, Z, dZ, aw, partials, s);
   }
   return use_bm192(pb) ? down_dgrad_impl<CfgB192>(pb, dY, Wd, Z, dZ, aw, partials, s)
                        : down_dgrad_impl<CfgB>(pb, dY, Wd, Z, dZ, aw, partials, s);
@@ -1648,8 +1651,9 @@ hipError_t launch_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const voi
     const hipError_t e = dma_gate_up_dgrad(pb, dZ, Wgu, dXp, s);
     if (e != hipSuccess) return e;
     const GemmProblem ps = small_experts(pb);
-    return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(ps, dZ, Wgu, dXp, s)
-                         : gate_up_dgrad_impl<CfgBW>(ps, dZ, Wgu, dXp, s);
+    if (use_bm192(pb)) return gate_up_dgrad_impl<CfgB192>(ps, dZ, Wgu, dXp, s);
+    return dma_small_enabled(pb) ? dma_gate_up_dgrad_small(ps, dZ, Wgu, dXp, s)
+                                 : gate_up_dgrad_impl<CfgBW>(ps, dZ, Wgu, dXp, s);
   }
   if (use_bm256(pb)) return gate_up_dgrad_impl<CfgB256>(pb, dZ, Wgu, dXp, s);
   return use_bm192(pb) ? gate_up_dgrad_impl<CfgB192>(pb, dZ, Wgu, dXp, s)

@@ -391,6 +391,15 @@ hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* 
 hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
                           float* partials, int nparts, hipStream_t s);
 hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s);
+// The experts of tile set 2 (ps = the problem with tile_set 2) on 128 x 256
+// tiles of the same engine, when H and I are multiples of 64.
+bool dma_small_enabled(const GemmProblem& pb);
+hipError_t dma_gate_up_small(const GemmProblem& ps, const void* X, const void* Wgu, void* a_out, void* z_out,
+                             hipStream_t s);
+hipError_t dma_down_small(const GemmProblem& ps, const void* a, const void* Wd, void* Yp, hipStream_t s);
+hipError_t dma_down_dgrad_small(const GemmProblem& ps, const void* dY, const void* Wd, const void* Z, void* dZ,
+                                void* aw, float* partials, int nparts, hipStream_t s);
+hipError_t dma_gate_up_dgrad_small(const GemmProblem& ps, const void* dZ, const void* Wgu, void* dXp, hipStream_t s);
 // weight gradients (dW[e] = A_e^T B_e) of the experts with more than hot_min positions
 bool dma_wgrad_enabled(const GemmProblem& pb);
 hipError_t dma_wgrad(const GemmProblem& pb, bool gate_up, const void* A, const void* B, void* dW, int hot_min,

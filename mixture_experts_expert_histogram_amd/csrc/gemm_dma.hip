@@ -101,6 +101,7 @@ struct DCfg {
 };
 using DCfgB = DCfg<256, 256, 2, 4, 5>;         // 5 stages of 32 k (160 KB)
 using DCfgB64 = DCfg<256, 256, 2, 4, 2, 64>;   // 2 stages of 64 k (128 KB)
+using DCfgS = DCfg<128, 256, 2, 4, 3, 64>;     // 3 stages of 64 k (144 KB), 128-row tiles
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt <= n and lgkmcnt = 0.
@@ -395,14 +396,20 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
 #define TILE_SYNC()                                        \
   if (jt != (int)(blockIdx.x >> 3)) lds_barrier();
 
-#define DMA_PROLOGUE(C)                                                              \
-  static_assert(C::NSTAGE >= 2 && C::NSTAGE <= 5, "ring of 2 to 5 stages");           \
-  __shared__ __attribute__((aligned(1024))) uint16_t S0[C::STAGE];                  \
-  __shared__ __attribute__((aligned(1024))) uint16_t S1[C::STAGE];                  \
-  __shared__ __attribute__((aligned(1024))) uint16_t S2[C::NSTAGE > 2 ? C::STAGE : 1]; \
-  __shared__ __attribute__((aligned(1024))) uint16_t S3[C::NSTAGE > 3 ? C::STAGE : 1]; \
-  __shared__ __attribute__((aligned(1024))) uint16_t S4[C::NSTAGE > 4 ? C::STAGE : 1]; \
-  uint16_t* const St[5] = {S0, S1, S2, S3, S4};                                     \
+// The stages are consecutive in one LDS array (the epilogue's 32 KB regions
+// cross stage boundaries when a stage is 48 KB).
+template <class C>
+struct alignas(1024) DmaLds {
+  uint16_t s[C::NSTAGE * C::STAGE];
+};
+
+#define DMA_PROLOGUE(C)                                                                   \
+  static_assert(C::NSTAGE >= 2 && C::NSTAGE <= 5, "ring of 2 to 5 stages");                \
+  static_assert(sizeof(DmaLds<C>) <= 160 * 1024, "the stages fit in LDS");                \
+  __shared__ DmaLds<C> lds;                                                              \
+  uint16_t* const St[5] = {lds.s, lds.s + 1 * C::STAGE, lds.s + (C::NSTAGE > 2 ? 2 : 0) * C::STAGE, \
+                           lds.s + (C::NSTAGE > 3 ? 3 : 0) * C::STAGE,                    \
+                           lds.s + (C::NSTAGE > 4 ? 4 : 0) * C::STAGE};                   \
   const int lane = threadIdx.x & 63;                                                \
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);                \
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -443,28 +450,31 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int epi_chunk(int row, int chunk) { return (row << 8) + ((chunk ^ (row & 15)) << 2); }
 
 template <class C>
-__device__ __forceinline__ void epi_r_to_lds(f32x16 (&acc)[C::FM][C::FN], float* const (&st)[4], int wn, int lane) {
-  static_assert(C::FM == 4 && C::BN == 256, "fragment fm of a 128-row half fills region fm");
+__device__ __forceinline__ void epi_r_to_lds(f32x16 (&acc)[C::FM][C::FN], float* const (&st)[4], int wm, int wn,
+                                             int lane) {
+  static_assert(C::BN == 256 && C::WM == 2 && (C::FM == 4 || C::FM == 2), "128-row passes of 256 columns");
   const int row = lane & 31;
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
+  for (int fm = 0; fm < C::FM; ++fm) {
+    // rows wm WTM + 32 fm .. +31 of the tile: region (wm FM + fm) % 4 of their pass
+    float* const reg = C::FM == 4 ? st[fm] : (wm == 0 ? st[fm] : st[2 + fm]);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
         const int chunk = (wn * C::WTN + fn * 32 + acc_col4(vg, lane)) >> 2;
-        *(float4*)(st[fm] + epi_chunk(row, chunk)) =
+        *(float4*)(reg + epi_chunk(row, chunk)) =
             make_float4(acc[fm][fn][vg * 4], acc[fm][fn][vg * 4 + 1], acc[fm][fn][vg * 4 + 2], acc[fm][fn][vg * 4 + 3]);
       }
+  }
 }
 
-// The four 32 KB regions of the stages: one per stage at BK = 32, two at 64.
+// The four 32 KB regions at the start of the stages.
 template <class C>
 __device__ __forceinline__ void epi_regions(uint16_t* const (&St)[5], float* (&st)[4]) {
-  constexpr int RPS = C::STAGE * 2 / 32768;
-  static_assert(RPS * 32768 == C::STAGE * 2 && 4 / RPS <= C::NSTAGE, "four 32 KB regions in the stages");
+  static_assert(C::NSTAGE * C::STAGE * 2 >= 4 * 32768, "four 32 KB regions in the stages");
 #pragma unroll
-  for (int q = 0; q < 4; ++q) st[q] = (float*)(St[q / RPS] + (q % RPS) * 16384);
+  for (int q = 0; q < 4; ++q) st[q] = (float*)(St[0] + q * 16384);
 }
 
 // Routing weights of the tile rows a wave takes in dma_epi_rows, one per lane
@@ -486,11 +496,11 @@ __device__ __forceinline__ float epi_row_weight(float wl, int tr) {
 template <class C, class RowFn>
 __device__ __forceinline__ void dma_epi_rows(f32x16 (&acc)[C::FM][C::FN], int rows, int wave, int wm, int wn,
                                              int lane, float* const (&st)[4], RowFn row) {
-  static_assert(C::NW == 8 && C::WM == 2, "8 waves over rows 8q + wave of a 128-row half");
+  static_assert(C::NW == 8 && C::WM == 2 && C::BM % 128 == 0, "8 waves over rows 8q + wave of a 128-row pass");
   lds_barrier();   // every wave's loads into the stages have landed (see pp_mainloop)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) epi_r_to_lds<C>(acc, st, wn, lane);
+  for (int h = 0; h < C::BM / 128; ++h) {   // 128-row passes: wave half h's rows, or the whole tile
+    if (C::BM == 128 || wm == h) epi_r_to_lds<C>(acc, st, wm, wn, lane);
     lds_barrier();
     const int hrows = rows - h * 128;
 #pragma unroll
@@ -502,7 +512,7 @@ __device__ __forceinline__ void dma_epi_rows(f32x16 (&acc)[C::FM][C::FN], int ro
         if (hr < hrows) row(h * 128 + hr, reg + ((hr & 31) << 8), hr & 15);
       }
     }
-    if (h == 0) lds_barrier();   // half 0 read before half 1 overwrites it
+    if (h + 1 < C::BM / 128) lds_barrier();   // half 0 read before half 1 overwrites it
   }
 }
 
@@ -617,7 +627,7 @@ template <class C, int RB>
 __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)[C::FM][C::FN], int m0, int rows,
                                                    int n0, int nt, int wave, int wm, int wn, int lane,
                                                    float* const (&st)[4]) {
-  static_assert(C::NW == 8 && C::WM == 2, "8 waves over rows 8q + wave of a 128-row half");
+  static_assert(C::NW == 8 && C::WM == 2 && C::BM % 128 == 0, "8 waves over rows 8q + wave of a 128-row pass");
   const int I = g.I, layout = g.layout;
   const float* Z = (const float*)g.Z;
   uint16_t* dZ = (uint16_t*)g.out0;
@@ -629,8 +639,8 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
   const float wl = epi_row_weights(g.w_of_pos, m0, rows, wave, lane);
   lds_barrier();   // every wave's loads into the stages have landed (see pp_mainloop)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) epi_r_to_lds<C>(acc, st, wn, lane);
+  for (int h = 0; h < C::BM / 128; ++h) {   // 128-row passes: wave half h's rows, or the whole tile
+    if (C::BM == 128 || wm == h) epi_r_to_lds<C>(acc, st, wm, wn, lane);
     lds_barrier();
     const int hrows = rows - h * 128;   // valid rows of this half (may be <= 0)
     if (hrows > 0) {
@@ -691,7 +701,7 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
         process(b, b & 1);
       }
     }
-    if (h == 0) lds_barrier();   // half 0 read before half 1 overwrites it
+    if (h + 1 < C::BM / 128) lds_barrier();   // half 0 read before half 1 overwrites it
   }
 }
 
@@ -860,17 +870,22 @@ int large_tile_min_slots(const GemmProblem& pb) { return dma_enabled(pb) ? kLarg
 // separate gate / up tensors) is a multiple of 64; 32-k stages otherwise.
 static bool dma_bk64(const GemmProblem& pb) { return pb.H % 64 == 0 && pb.I % 64 == 0; }
 
-template <class C>
-static hipError_t dma_gate_up_impl(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
-                                   hipStream_t s) {
+// The launchers take the problem with its tile set chosen (1: the experts of
+// the 256-row tiles, 2: the others) and the kernel's timing name.
+static GemmProblem big_experts(const GemmProblem& pb) {
   GemmProblem p = pb;
   p.tile_set = 1;
-  GArgs g = base_args(p, C::BM);
+  return p;
+}
+
+template <class C>
+static hipError_t dma_gate_up_impl(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
+                                   const char* name, hipStream_t s) {
+  GArgs g = base_args(pb, C::BM);
   g.A = X; g.B = Wgu; g.out0 = a_out; g.out1 = z_out;
   set_gu(g, pb, Wgu, nullptr, 0);
   g.ntn = (pb.I + C::BN / 2 - 1) / (C::BN / 2);
   const long grid = persistent_grid();
-  const char* name = a_out ? "gate_up_glu_big" : "gate_up_z_big";
   return run_kernel(name, s, [&] {
     if (a_out && z_out) dma_gate_up_kernel<C, true, true><<<grid, C::NT, 0, s>>>(g);
     else if (a_out) dma_gate_up_kernel<C, true, false><<<grid, C::NT, 0, s>>>(g);
@@ -880,60 +895,81 @@ static hipError_t dma_gate_up_impl(const GemmProblem& pb, const void* X, const v
 
 hipError_t dma_gate_up(const GemmProblem& pb, const void* X, const void* Wgu, void* a_out, void* z_out,
                        hipStream_t s) {
-  return dma_bk64(pb) ? dma_gate_up_impl<DCfgB64>(pb, X, Wgu, a_out, z_out, s)
-                      : dma_gate_up_impl<DCfgB>(pb, X, Wgu, a_out, z_out, s);
+  const char* name = a_out ? "gate_up_glu_big" : "gate_up_z_big";
+  return dma_bk64(pb) ? dma_gate_up_impl<DCfgB64>(big_experts(pb), X, Wgu, a_out, z_out, name, s)
+                      : dma_gate_up_impl<DCfgB>(big_experts(pb), X, Wgu, a_out, z_out, name, s);
 }
 
 template <class C>
-static hipError_t dma_down_impl(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
-  GemmProblem p = pb;
-  p.tile_set = 1;
-  GArgs g = base_args(p, C::BM);
+static hipError_t dma_down_impl(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, const char* name,
+                                hipStream_t s) {
+  GArgs g = base_args(pb, C::BM);
   g.A = a; g.B = Wd; g.out0 = Yp;
   g.ntn = (pb.H + C::BN - 1) / C::BN;
   const long grid = persistent_grid();
-  return run_kernel("down_weighted_big", s, [&] { dma_down_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+  return run_kernel(name, s, [&] { dma_down_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
 hipError_t dma_down(const GemmProblem& pb, const void* a, const void* Wd, void* Yp, hipStream_t s) {
-  return dma_bk64(pb) ? dma_down_impl<DCfgB64>(pb, a, Wd, Yp, s) : dma_down_impl<DCfgB>(pb, a, Wd, Yp, s);
+  const char* name = "down_weighted_big";
+  return dma_bk64(pb) ? dma_down_impl<DCfgB64>(big_experts(pb), a, Wd, Yp, name, s)
+                      : dma_down_impl<DCfgB>(big_experts(pb), a, Wd, Yp, name, s);
 }
 
 template <class C>
 static hipError_t dma_down_dgrad_impl(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ,
-                                      void* aw, float* partials, int nparts, hipStream_t s) {
-  GemmProblem p = pb;
-  p.tile_set = 1;
-  GArgs g = base_args(p, C::BM);
+                                      void* aw, float* partials, int nparts, const char* name, hipStream_t s) {
+  GArgs g = base_args(pb, C::BM);
   g.A = dY; g.B = Wd; g.Z = Z; g.out0 = dZ; g.out1 = aw; g.partials = partials;
   g.ntn = (pb.I + C::BN - 1) / C::BN;
   g.nparts = nparts;
   const long grid = persistent_grid();
-  return run_kernel("down_dgrad_glu_bwd_big", s, [&] { dma_down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+  return run_kernel(name, s, [&] { dma_down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
 hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
                           float* partials, int nparts, hipStream_t s) {
-  return dma_bk64(pb) ? dma_down_dgrad_impl<DCfgB64>(pb, dY, Wd, Z, dZ, aw, partials, nparts, s)
-                      : dma_down_dgrad_impl<DCfgB>(pb, dY, Wd, Z, dZ, aw, partials, nparts, s);
+  const char* name = "down_dgrad_glu_bwd_big";
+  return dma_bk64(pb) ? dma_down_dgrad_impl<DCfgB64>(big_experts(pb), dY, Wd, Z, dZ, aw, partials, nparts, name, s)
+                      : dma_down_dgrad_impl<DCfgB>(big_experts(pb), dY, Wd, Z, dZ, aw, partials, nparts, name, s);
 }
 
 template <class C>
 static hipError_t dma_gate_up_dgrad_impl(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp,
-                                         hipStream_t s) {
-  GemmProblem p = pb;
-  p.tile_set = 1;
-  GArgs g = base_args(p, C::BM);
+                                         const char* name, hipStream_t s) {
+  GArgs g = base_args(pb, C::BM);
   g.A = dZ; g.B = Wgu; g.out0 = dXp;
   set_gu(g, pb, Wgu, nullptr, 0);
   g.ntn = (pb.H + C::BN - 1) / C::BN;
   const long grid = persistent_grid();
-  return run_kernel("gate_up_dgrad_big", s, [&] { dma_gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+  return run_kernel(name, s, [&] { dma_gate_up_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
 }
 
 hipError_t dma_gate_up_dgrad(const GemmProblem& pb, const void* dZ, const void* Wgu, void* dXp, hipStream_t s) {
-  return dma_bk64(pb) ? dma_gate_up_dgrad_impl<DCfgB64>(pb, dZ, Wgu, dXp, s)
-                      : dma_gate_up_dgrad_impl<DCfgB>(pb, dZ, Wgu, dXp, s);
+  const char* name = "gate_up_dgrad_big";
+  return dma_bk64(pb) ? dma_gate_up_dgrad_impl<DCfgB64>(big_experts(pb), dZ, Wgu, dXp, name, s)
+                      : dma_gate_up_dgrad_impl<DCfgB>(big_experts(pb), dZ, Wgu, dXp, name, s);
+}
+
+// The experts of the other engine's 128-row tiles (tile set 2) on 128 x 256
+// tiles of this engine: three stages of 64 k (48 KB each), the same
+// ping-pong with 64 x 64 per wave.  H and I multiples of 64.
+bool dma_small_enabled(const GemmProblem& pb) { return dma_enabled(pb) && dma_bk64(pb); }
+
+hipError_t dma_gate_up_small(const GemmProblem& ps, const void* X, const void* Wgu, void* a_out, void* z_out,
+                             hipStream_t s) {
+  return dma_gate_up_impl<DCfgS>(ps, X, Wgu, a_out, z_out, a_out ? "gate_up_glu" : "gate_up_z", s);
+}
+hipError_t dma_down_small(const GemmProblem& ps, const void* a, const void* Wd, void* Yp, hipStream_t s) {
+  return dma_down_impl<DCfgS>(ps, a, Wd, Yp, "down_weighted", s);
+}
+hipError_t dma_down_dgrad_small(const GemmProblem& ps, const void* dY, const void* Wd, const void* Z, void* dZ,
+                                void* aw, float* partials, int nparts, hipStream_t s) {
+  return dma_down_dgrad_impl<DCfgS>(ps, dY, Wd, Z, dZ, aw, partials, nparts, "down_dgrad_glu_bwd", s);
+}
+hipError_t dma_gate_up_dgrad_small(const GemmProblem& ps, const void* dZ, const void* Wgu, void* dXp,
+                                   hipStream_t s) {
+  return dma_gate_up_dgrad_impl<DCfgS>(ps, dZ, Wgu, dXp, "gate_up_dgrad", s);
 }
 
 // Weight gradients of the experts with more than hot_min positions; every

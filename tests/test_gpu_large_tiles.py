@@ -56,6 +56,23 @@ def test_large_tile_experts_64k_stages(act, layout):
     run_and_compare(inp, save=act == "clamped", grad_dtype="bf16", poison=True)
 
 
+@pytest.mark.parametrize("act,layout", [("clamped", "interleaved"), ("swiglu", "concat")])
+@pytest.mark.parametrize("save", [True, False])
+def test_small_experts_64k_stages(act, layout, save):
+    """H = 320 and I = 192 with the batch averaging 293 slots per expert: the
+    experts of 1-300 slots (all but the 1300-slot one) take the same engine's
+    128 x 256 tiles (three 64-k stages; 300 slots: two full tiles and one of
+    44 rows), N ragged in every product as above."""
+    counts = [1300, 300, 260, 257, 128, 100, 1, 0]
+    E, K = len(counts), 1
+    T = sum(counts)
+    assert T // E > 176
+    rng = np.random.default_rng(73)
+    ids = rng.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
+    inp = small_inputs(T, 320, 192, E, K, "bf16", act, layout, seed=73, ids=ids)
+    run_and_compare(inp, save=save, grad_dtype="bf16", poison=True)
+
+
 @pytest.mark.parametrize("layout", ["interleaved", "concat"])
 def test_large_tile_separate_weights(layout):
     check_separate(large_tile_inputs("swiglu", layout, 53), "swiglu", layout, "bf16", "fp32", True)
