@@ -111,14 +111,15 @@ LARGE_MIN = 512  # experts with at least this many slots take the 256-row token-
 def large_tile_experts(wl, counts):
     """Experts the library runs on the 256-row tiles: from LARGE_MIN slots on,
     and below that those whose 256-row tiles hold no more rows than the other
-    engine's tiles (192 rows when the batch averages 101-176 slots per
-    expert, else 128) would."""
+    tiles (192 rows when the batch averages 101-176 slots per expert and H or
+    I is not a multiple of 64, else 128) would."""
     import numpy as np
     counts = np.asarray(counts)
     if not large_tiles(wl):
         return np.zeros(len(counts), dtype=bool)
     mean = wl.S // wl.E if wl.E else 0
-    bms = 192 if 100 < mean <= 176 else 128
+    dma_small = large_tiles(wl) and wl.H % 64 == 0 and wl.I % 64 == 0   # the small experts' 128-row DMA tiles
+    bms = 192 if 100 < mean <= 176 and not dma_small else 128
     rows_big = (counts + 255) // 256 * 256
     rows_small = (counts + bms - 1) // bms * bms
     return (counts >= LARGE_MIN) | ((counts > 0) & (rows_big <= rows_small))
