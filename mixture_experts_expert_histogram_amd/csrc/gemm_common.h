@@ -25,32 +25,49 @@ template <> __device__ __forceinline__ void store_val<uint16_t>(uint16_t* p, flo
 }
 template <> __device__ __forceinline__ void store_val<float>(float* p, float v) { *p = v; }
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+// The logistic function through the hardware reciprocal (v_rcp_f32, about
+// 1 ulp) rather than a correctly rounded division: every value it feeds is
+// rounded to bf16 or summed in fp32 afterwards.
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-// Gated activation (SwiGLU, or the clamped GLU of the gpt-oss-shaped pages).
-__device__ __forceinline__ float glu_fwd(float g, float u, int act, float L, float al) {
-  if (act == 0) return g * sigmoid_f(g) * u;
-  const float gc = fminf(g, L);
-  const float uc = fminf(fmaxf(u, -L), L);
-  return (uc + 1.f) * gc * sigmoid_f(al * gc);
+// Gated activation (SwiGLU, ACT = 0, or the clamped GLU of the gpt-oss-shaped
+// pages, ACT = 1), with the kind fixed at compile time.
+template <int ACT>
+__device__ __forceinline__ float glu_fwd_t(float g, float u, float L, float al) {
+  if constexpr (ACT == 0) {
+    return g * sigmoid_f(g) * u;
+  } else {
+    const float gc = __builtin_amdgcn_fmed3f(g, -__builtin_inff(), L);   // min(g, L)
+    const float uc = __builtin_amdgcn_fmed3f(u, -L, L);
+    return (uc + 1.f) * gc * sigmoid_f(al * gc);
+  }
 }
 // Returns a = phi(g,u) and (dg, du) = phi'(g,u) * da.
-__device__ __forceinline__ float glu_bwd(float g, float u, float da, int act, float L, float al, float& dg,
-                                         float& du) {
-  if (act == 0) {
+template <int ACT>
+__device__ __forceinline__ float glu_bwd_t(float g, float u, float da, float L, float al, float& dg, float& du) {
+  if constexpr (ACT == 0) {
     const float s = sigmoid_f(g);
     const float silu = g * s;
     dg = da * u * s * (1.f + g * (1.f - s));
     du = da * silu;
     return silu * u;
+  } else {
+    const float gc = __builtin_amdgcn_fmed3f(g, -__builtin_inff(), L);   // min(g, L)
+    const float uc = __builtin_amdgcn_fmed3f(u, -L, L);
+    const float s = sigmoid_f(al * gc);
+    const float q = gc * s;
+    dg = (g <= L) ? da * (uc + 1.f) * s * (1.f + al * gc * (1.f - s)) : 0.f;
+    du = (uc == u) ? da * q : 0.f;   // u inside [-L, L]
+    return (uc + 1.f) * q;
   }
-  const float gc = fminf(g, L);
-  const float uc = fminf(fmaxf(u, -L), L);
-  const float s = sigmoid_f(al * gc);
-  const float q = gc * s;
-  dg = (g <= L) ? da * (uc + 1.f) * s * (1.f + al * gc * (1.f - s)) : 0.f;
-  du = (u >= -L && u <= L) ? da * q : 0.f;
-  return (uc + 1.f) * q;
+}
+// The same with the kind chosen at run time (act = 0 or 1).
+__device__ __forceinline__ float glu_fwd(float g, float u, int act, float L, float al) {
+  return act == 0 ? glu_fwd_t<0>(g, u, L, al) : glu_fwd_t<1>(g, u, L, al);
+}
+__device__ __forceinline__ float glu_bwd(float g, float u, float da, int act, float L, float al, float& dg,
+                                         float& du) {
+  return act == 0 ? glu_bwd_t<0>(g, u, da, L, al, dg, du) : glu_bwd_t<1>(g, u, da, L, al, dg, du);
 }
 
 // The MFMA is issued with the B fragment first, so it computes the tile

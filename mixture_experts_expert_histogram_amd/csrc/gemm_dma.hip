@@ -40,6 +40,8 @@
 // ds_read_b64_tr_b16, like the other engine's.  K must be a multiple of BK
 // (the weight gradients' ragged k is handled by clamped rows and zeroed LDS
 // rows).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -519,7 +521,7 @@ __device__ __forceinline__ void dma_epi_rows(f32x16 (&acc)[C::FM][C::FN], int ro
 // ---------------------------------------------------------------- gate_up fwd
 // B rows: 32-row groups alternate gate and up rows of the same 32 activation
 // columns (see epi_gate_up).
-template <class C, bool WRITE_A, bool WRITE_Z>
+template <class C, bool WRITE_A, bool WRITE_Z, int ACT, int LAYOUT>
 __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
   DMA_PROLOGUE(C)
   TILE_LOOP(C) {
@@ -559,11 +561,11 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
       if (!col_ok) return;
       const size_t p = (size_t)(m0 + tr);
       if (WRITE_A)
-        *(uint32_t*)(a_out + p * I + j) = pack_bf16(glu_fwd(gv.x, uv.x, g.act, g.limit, g.alpha),
-                                                    glu_fwd(gv.y, uv.y, g.act, g.limit, g.alpha));
+        *(uint32_t*)(a_out + p * I + j) = pack_bf16(glu_fwd_t<ACT>(gv.x, uv.x, g.limit, g.alpha),
+                                                    glu_fwd_t<ACT>(gv.y, uv.y, g.limit, g.alpha));
       if (WRITE_Z) {
         float* zr = z_out + p * 2 * I;
-        if (g.layout) {
+        if constexpr (LAYOUT) {
           *(float4*)(zr + 2 * j) = make_float4(gv.x, uv.x, gv.y, uv.y);
         } else {
           *(float2*)(zr + j) = gv;
@@ -616,19 +618,37 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
 // move as one contiguous access per row and wave, in batches of 2 rows with
 // the next batch's Z loads in flight.
 
-// Z of one row at columns ic .. ic + 3 (interleaved: g, u pairs over 8 floats;
-// concatenated: gate, then up at + I).
-__device__ __forceinline__ void epi_z_load(const float* zr, int ic, int I, int layout, float4& z0, float4& z1) {
-  z0 = *(const float4*)(zr + (layout ? 2 * ic : ic));
-  z1 = *(const float4*)(zr + (layout ? 2 * ic + 4 : I + ic));
+// Sum of the 16 lanes of each DPP row, in every lane of the row: quad
+// sums (quad_perm 1,0,3,2 then 2,3,0,1), then the half-row and row mirrors.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_sum16(float x) {
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-template <class C, int RB>
+// Z of one row at columns ic .. ic + 3 (interleaved: g, u pairs over 8 floats;
+// concatenated: gate, then up at + I).
+template <int LAYOUT>
+__device__ __forceinline__ void epi_z_load(const float* zr, int ic, int I, float4& z0, float4& z1) {
+  z0 = *(const float4*)(zr + (LAYOUT ? 2 * ic : ic));
+  z1 = *(const float4*)(zr + (LAYOUT ? 2 * ic + 4 : I + ic));
+}
+
+template <class C, int RB, int ACT, int LAYOUT>
 __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)[C::FM][C::FN], int m0, int rows,
                                                    int n0, int nt, int wave, int wm, int wn, int lane,
                                                    float* const (&st)[4]) {
   static_assert(C::NW == 8 && C::WM == 2 && C::BM % 128 == 0, "8 waves over rows 8q + wave of a 128-row pass");
-  const int I = g.I, layout = g.layout;
+  const int I = g.I;
   const float* Z = (const float*)g.Z;
   uint16_t* dZ = (uint16_t*)g.out0;
   uint16_t* aw = (uint16_t*)g.out1;
@@ -649,7 +669,7 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
       auto load = [&](int b, int buf) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
-          epi_z_load(Z + (size_t)pos(b * RB + r) * 2 * I, ic, I, layout, za[buf][r], zb[buf][r]);
+          epi_z_load<LAYOUT>(Z + (size_t)pos(b * RB + r) * 2 * I, ic, I, za[buf][r], zb[buf][r]);
       };
       auto process = [&](int b, int buf) {
 #pragma unroll
@@ -660,7 +680,7 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
           const float4 rv = *(const float4*)(st[q >> 2] + epi_chunk(hr & 31, lane));
           const float4 z0 = za[buf][r], z1 = zb[buf][r];
           float gv[4], uv[4];
-          if (layout) {
+          if constexpr (LAYOUT) {
             gv[0] = z0.x; uv[0] = z0.y; gv[1] = z0.z; uv[1] = z0.w;
             gv[2] = z1.x; uv[2] = z1.y; gv[3] = z1.z; uv[3] = z1.w;
           } else {
@@ -671,17 +691,19 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
           float dg[4], du[4], a[4], rs = 0.f;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            a[c] = glu_bwd(gv[c], uv[c], w * rr[c], g.act, g.limit, g.alpha, dg[c], du[c]);
+            a[c] = glu_bwd_t<ACT>(gv[c], uv[c], w * rr[c], g.limit, g.alpha, dg[c], du[c]);
             rs += rr[c] * a[c];
           }
           if (!col_ok) rs = 0.f;   // columns past I hold clamped weight columns
-          // sum over the 32 lanes of each 128-column slot, in a fixed order
-#pragma unroll
-          for (int d = 16; d >= 1; d >>= 1) rs += __shfl_xor(rs, d);
+          // sum over the 32 lanes of each 128-column slot, in a fixed order:
+          // 16-lane row sums by DPP, then lanes 0 + 16 and 32 + 48
+          rs = dpp_row_sum16(rs);
+          const float rs_lo = readlane_f(rs, 0) + readlane_f(rs, 16), rs_hi = readlane_f(rs, 32) + readlane_f(rs, 48);
+          rs = lane < 32 ? rs_lo : rs_hi;
           if (hr < hrows) {
             uint16_t* dzr = dZ + p * 2 * I;
             if (col_ok) {
-              if (layout) {
+              if constexpr (LAYOUT) {
                 store4x2<uint16_t>(dzr + 2 * i, dg, du);
               } else {
                 store4<uint16_t>(dzr + i, dg[0], dg[1], dg[2], dg[3]);
@@ -706,7 +728,7 @@ __device__ __forceinline__ void dma_epi_down_dgrad(const GArgs& g, f32x16 (&acc)
 }
 
 // r[p, i] = sum_h dYp[p, h] Wd[e][h, i]: the weights are k (= h) rows of I columns.
-template <class C>
+template <class C, int ACT, int LAYOUT>
 __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
   DMA_PROLOGUE(C)
   TILE_LOOP(C) {
@@ -726,7 +748,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
     pp_mainloop<C, false, true>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
     float* st[4];
     epi_regions<C>(St, st);
-    dma_epi_down_dgrad<C, 2>(g, acc, m0, rows, n0, nt, wave, wm, wn, lane, st);
+    dma_epi_down_dgrad<C, 2, ACT, LAYOUT>(g, acc, m0, rows, n0, nt, wave, wm, wn, lane, st);
   }
 }
 
@@ -870,6 +892,22 @@ int large_tile_min_slots(const GemmProblem& pb) { return dma_enabled(pb) ? kLarg
 // separate gate / up tensors) is a multiple of 64; 32-k stages otherwise.
 static bool dma_bk64(const GemmProblem& pb) { return pb.H % 64 == 0 && pb.I % 64 == 0; }
 
+// f(A, L) with the activation kind and the gate / up layout of the problem
+// as compile-time constants (A::value, L::value), so that the epilogues that
+// use them are instantiated per kind instead of branching per element.
+template <class F>
+static void act_layout(const GemmProblem& pb, F&& f) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (pb.act) {
+    if (pb.layout) f(I1{}, I1{});
+    else f(I1{}, I0{});
+  } else {
+    if (pb.layout) f(I0{}, I1{});
+    else f(I0{}, I0{});
+  }
+}
+
 // The launchers take the problem with its tile set chosen (1: the experts of
 // the 256-row tiles, 2: the others) and the kernel's timing name.
 static GemmProblem big_experts(const GemmProblem& pb) {
@@ -887,9 +925,11 @@ static hipError_t dma_gate_up_impl(const GemmProblem& pb, const void* X, const v
   g.ntn = (pb.I + C::BN / 2 - 1) / (C::BN / 2);
   const long grid = persistent_grid();
   return run_kernel(name, s, [&] {
-    if (a_out && z_out) dma_gate_up_kernel<C, true, true><<<grid, C::NT, 0, s>>>(g);
-    else if (a_out) dma_gate_up_kernel<C, true, false><<<grid, C::NT, 0, s>>>(g);
-    else dma_gate_up_kernel<C, false, true><<<grid, C::NT, 0, s>>>(g);
+    act_layout(pb, [&](auto A, auto L) {
+      if (a_out && z_out) dma_gate_up_kernel<C, true, true, A.value, L.value><<<grid, C::NT, 0, s>>>(g);
+      else if (a_out) dma_gate_up_kernel<C, true, false, A.value, L.value><<<grid, C::NT, 0, s>>>(g);
+      else dma_gate_up_kernel<C, false, true, A.value, L.value><<<grid, C::NT, 0, s>>>(g);
+    });
   });
 }
 
@@ -924,7 +964,9 @@ static hipError_t dma_down_dgrad_impl(const GemmProblem& pb, const void* dY, con
   g.ntn = (pb.I + C::BN - 1) / C::BN;
   g.nparts = nparts;
   const long grid = persistent_grid();
-  return run_kernel(name, s, [&] { dma_down_dgrad_kernel<C><<<grid, C::NT, 0, s>>>(g); });
+  return run_kernel(name, s, [&] {
+    act_layout(pb, [&](auto A, auto L) { dma_down_dgrad_kernel<C, A.value, L.value><<<grid, C::NT, 0, s>>>(g); });
+  });
 }
 
 hipError_t dma_down_dgrad(const GemmProblem& pb, const void* dY, const void* Wd, const void* Z, void* dZ, void* aw,
