@@ -1297,15 +1297,29 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
   // Store q (0..NQ-1) of the pending block: RPI staged rows, CPRS lanes per
   // row, one whole row segment (128 bytes bf16, 256 fp32) each, non-temporal
   // (dW is not read again here, so it need not displace the operand tiles in
-  // L2).
+  // L2).  The lane's row pointer and bounds are formed once per block (pbase:
+  // row pj*64 + lane / CPRS at the lane's column; rows q RPI further on are
+  // N elements apart), so a store costs one address add; separate gate / up
+  // tensors map each row on its own.
   constexpr int RPI = 64 / CPRS, NQ = 64 / RPI, VPC = 16 / (int)sizeof(OutT);
   constexpr int NQI = NQ < 8 ? NQ : 8;   // stores issued between k-slices; the rest after them
+  OutT* pbase = dW;
+  int prows = 0;   // rows of the pending block from the lane's first row to M, 0 if its column is past N
+  auto set_pending = [&](int e, int j, int n0) {
+    const int r0 = lane / CPRS, n = n0 + wave * 64 + (lane % CPRS) * VPC;
+    pe = e; pj = j; pn0 = n0;
+    prows = n < N ? M - (j * kResM + r0) : 0;
+    pbase = dW + ((size_t)e * M + j * kResM + r0) * N + n;
+  };
   auto store_step = [&](int q) {
     const int r = q * RPI + lane / CPRS, c = lane % CPRS;
     const uint4 v = *(const uint4*)(pst + stage_off(r, c));
-    const int m = pj * kResM + r, n = pn0 + wave * 64 + c * VPC;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    if (m < M && n < N) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)(row_ptr(pe, m) + n));
+    if (q * RPI < prows) {
+      OutT* dst = pbase + (size_t)q * RPI * N;
+      if (GATE_UP && g.gu_sep) dst = row_ptr(pe, pj * kResM + r) + pn0 + wave * 64 + c * VPC;
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)dst);
+    }
   };
   // Experts without positions first (zeros in whole 16-byte chunks, no LDS),
   // while no resident operand is live.
@@ -1363,9 +1377,7 @@ __global__ __launch_bounds__(kResThreads, 1) void wgrad_res_kernel(GArgs g) {
       char* st = stage + (BF && pst == stage ? STAGE_BUF : 0);
       stage_acc(st);
       pst = st;
-      pe = it.e;
-      pj = j;
-      pn0 = it.n0;
+      set_pending(it.e, j, it.n0);
       pending = true;
     }
   }
