@@ -155,19 +155,12 @@ constexpr int kRowTileGroup = 8;
 
 // Token-row tiles: (expert, N-tile, M-tile of BM rows), ordered by expert,
 // then by groups of M-tiles, then N-tile, then M-tile, so the M-tiles of one
-// expert that share a weight tile are neighbours.  The grid is sized for the worst case; the actual tile
-// count is read from the routing tables and split into 8 equal contiguous
-// ranges, one per XCD (hardware deals workgroup b to XCD b % 8).  Returns
-// false for a workgroup without a tile.
+// expert that share a weight tile are neighbours.  row_tile_of decodes tile t
+// of that order (t below the total, tile_prefix[E] * ntn).
 template <int BM>
-__device__ __forceinline__ bool row_tile_at(const GArgs& g, int xcd, int j, int& e, int& m0, int& rows, int& nt) {
+__device__ __forceinline__ void row_tile_of(const GArgs& g, int t, int& e, int& m0, int& rows, int& nt) {
   const int* tp = g.tile_prefix;
   const int ntn = g.ntn;
-  const int total = tp[g.E] * ntn;
-  const int per = (total + 7) >> 3;
-  if (j >= per) return false;
-  const int t = xcd * per + j;
-  if (t >= total) return false;
   const int q = t / ntn;
   int lo = 0, hi = g.E;            // largest e with tp[e] <= q
   while (lo < hi) {
@@ -192,6 +185,20 @@ __device__ __forceinline__ bool row_tile_at(const GArgs& g, int xcd, int j, int&
   const int mt = grp * kRowTileGroup + (rem - nt * gm);
   m0 = g.offsets[e] + mt * BM;
   rows = min(BM, g.offsets[e + 1] - m0);
+}
+
+// The grid of one workgroup per tile is sized for the worst case; the actual
+// tile count is read from the routing tables and split into 8 equal
+// contiguous ranges, one per XCD (hardware deals workgroup b to XCD b % 8).
+// Returns false for a workgroup without a tile.
+template <int BM>
+__device__ __forceinline__ bool row_tile_at(const GArgs& g, int xcd, int j, int& e, int& m0, int& rows, int& nt) {
+  const int total = g.tile_prefix[g.E] * g.ntn;
+  const int per = (total + 7) >> 3;
+  if (j >= per) return false;
+  const int t = xcd * per + j;
+  if (t >= total) return false;
+  row_tile_of<BM>(g, t, e, m0, rows, nt);
   return true;
 }
 

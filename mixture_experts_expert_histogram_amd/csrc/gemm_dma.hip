@@ -385,14 +385,33 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 }
 
-// Persistent workgroups, one per CU: workgroup b walks tiles b / 8,
-// b / 8 + gridDim / 8, ... of XCD b % 8's contiguous range of the tile table
-// (TILE_LOOP).  The barrier between tiles keeps a tile's first loads out of
-// stages that slower waves may still be reading for the previous one (its
-// epilogue included); every wave's own loads have landed before it.
-#define TILE_LOOP(C)                                                                          \
-  int e, m0, rows, nt;                                                                        \
-  for (int jt = blockIdx.x >> 3; row_tile_at<C::BM>(g, blockIdx.x & 7, jt, e, m0, rows, nt); \
+// Persistent workgroups, one per CU, over the token-row tile order: chunks
+// of 32 consecutive tiles (an XCD's 32 workgroups, 4 N-tiles of a group of
+// 8 M-tiles) are dealt round-robin to the XCDs, and workgroup b walks
+// positions b / 8, b / 8 + gridDim / 8, ... of XCD b % 8's chunks
+// (TILE_LOOP).  So the 8 XCDs work on neighbouring chunks of one expert at
+// once and miss in their L2s on the same token rows and weight tiles at
+// about the same time, which the last-level cache can then serve to all but
+// the first; with 8 equal contiguous ranges each XCD streamed its own
+// experts (Zipf batch: step 23.15 -> 22.10 ms, the token-row kernels of the
+// 256-row tiles 5-9 % faster; chunks of 16 and 64 measured 22.2 and
+// 22.55 ms).  A position's
+// tile index grows with the position, so the first past the end ends the
+// walk.  The barrier between tiles keeps a tile's first loads out of stages
+// that slower waves may still be reading for the previous one (its epilogue
+// included); every wave's own loads have landed before it.
+constexpr int kTileChunk = 32;
+template <int BM>
+__device__ __forceinline__ bool row_tile_dealt(const GArgs& g, int xcd, int j, int& e, int& m0, int& rows, int& nt) {
+  const int t = ((j / kTileChunk) * 8 + xcd) * kTileChunk + j % kTileChunk;
+  if (t >= g.tile_prefix[g.E] * g.ntn) return false;
+  row_tile_of<BM>(g, t, e, m0, rows, nt);
+  return true;
+}
+
+#define TILE_LOOP(C)                                                                              \
+  int e, m0, rows, nt;                                                                            \
+  for (int jt = blockIdx.x >> 3; row_tile_dealt<C::BM>(g, blockIdx.x & 7, jt, e, m0, rows, nt); \
        jt += gridDim.x >> 3)
 
 #define TILE_SYNC()                                        \
