@@ -42,7 +42,12 @@ def test_large_tile_experts_match_oracle(act, layout, save):
     run_and_compare(large_tile_inputs(act, layout, 51), save=save, grad_dtype="bf16", poison=True)
 
 
-@pytest.mark.parametrize("act,layout", [("clamped", "interleaved"), ("swiglu", "concat")])
+# The GLU epilogues are compiled per activation kind and gate / up layout:
+# every combination runs through both tile sizes of the large-tile engine.
+ALL_GLU = [("clamped", "interleaved"), ("swiglu", "concat"), ("clamped", "concat"), ("swiglu", "interleaved")]
+
+
+@pytest.mark.parametrize("act,layout", ALL_GLU)
 def test_large_tile_experts_64k_stages(act, layout):
     """H = 320 and I = 192 (multiples of 64): the token-row kernels take
     stages of 64 k (gate_up 5 stages, an odd count for the two-stage ring;
@@ -56,7 +61,7 @@ def test_large_tile_experts_64k_stages(act, layout):
     run_and_compare(inp, save=act == "clamped", grad_dtype="bf16", poison=True)
 
 
-@pytest.mark.parametrize("act,layout", [("clamped", "interleaved"), ("swiglu", "concat")])
+@pytest.mark.parametrize("act,layout", ALL_GLU)
 @pytest.mark.parametrize("save", [True, False])
 def test_small_experts_64k_stages(act, layout, save):
     """H = 320 and I = 192 with the batch averaging 293 slots per expert: the
