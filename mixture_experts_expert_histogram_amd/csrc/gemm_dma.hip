@@ -104,6 +104,12 @@ struct DCfg {
 using DCfgB = DCfg<256, 256, 2, 4, 5>;         // 5 stages of 32 k (160 KB)
 using DCfgB64 = DCfg<256, 256, 2, 4, 2, 64>;   // 2 stages of 64 k (128 KB)
 using DCfgS = DCfg<128, 256, 2, 4, 3, 64>;     // 3 stages of 64 k (144 KB), 128-row tiles
+// The weight gradients: 4 stages of 32 k (128 KB, the least the LDS epilogue
+// needs).  Both operands already load whole 256-byte row segments at 32 k; against
+// 5 stages the Zipf batch's dW_gate_up took 4.17 ms instead of 4.21 and the
+// backward workload's (experts of ~250-500 positions) 3.33 instead of 3.48;
+// two 64-k stages were faster only at short k (4.43 on Zipf, 3.23).
+using DCfgW = DCfg<256, 256, 2, 4, 4>;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt <= n and lgkmcnt = 0.
@@ -1043,7 +1049,7 @@ bool dma_wgrad_enabled(const GemmProblem& pb) {
 template <bool GU, typename OutT>
 static hipError_t dma_wgrad_impl(const GemmProblem& pb, const void* A, const void* B, void* dW, int hot_min,
                                  hipStream_t s) {
-  using C = DCfgB;
+  using C = DCfgW;
   const int M = GU ? 2 * pb.I : pb.H, N = GU ? pb.H : pb.I;
   GArgs g = base_args(pb, C::BM);
   g.A = A; g.B = B; g.out0 = dW;
