@@ -77,9 +77,21 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int b
   const int te = threadIdx.x % E, ts = threadIdx.x / E;
   const bool slice_thread = threadIdx.x < slices * E;
   const int b0 = ts * per, b1 = min(nblk, b0 + per);
+  // The chunk loops load 8 entries before using any, so a thread waits for
+  // one round trip per 8 chunks rather than per chunk (the sums are integer,
+  // so the grouping changes nothing).
+  constexpr int U = 8;
   if (slice_thread) {
     int sum = 0;
-    for (int b = b0; b < b1; ++b) sum += blk_hist[(size_t)b * E + te];
+    int b = b0;
+    for (; b + U <= b1; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = blk_hist[(size_t)(b + u) * E + te];
+#pragma unroll
+      for (int u = 0; u < U; ++u) sum += v[u];
+    }
+    for (; b < b1; ++b) sum += blk_hist[(size_t)b * E + te];
     part[threadIdx.x] = sum;
   }
   __syncthreads();
@@ -101,7 +113,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int b
   __syncthreads();
   if (slice_thread) {   // per-chunk bases of the expert's slots, chunk by chunk
     int run = base[te] + part[threadIdx.x];
-    for (int b = b0; b < b1; ++b) {
+    int b = b0;
+    for (; b + U <= b1; b += U) {
+      int h[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) h[u] = blk_hist[(size_t)(b + u) * E + te];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        blk_hist[(size_t)(b + u) * E + te] = run;
+        run += h[u];
+      }
+    }
+    for (; b < b1; ++b) {
       const int h = blk_hist[(size_t)b * E + te];
       blk_hist[(size_t)b * E + te] = run;
       run += h;
@@ -126,17 +149,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int b
   }
   // Slots with an id outside [0,E) go after every valid slot, chunk by chunk
   // in slot order, so positions [offsets[E], S) hold them and every position
-  // names a real slot and token: blk_bad becomes each chunk's first position.
-  if (threadIdx.x == 0) {
-    const int valid = base[E - 1] + cnt[E - 1];
-    int run = valid;
-    for (int b = 0; b < nblk; ++b) {
-      const int h = blk_bad[b];
-      blk_bad[b] = run;
-      run += h;
-    }
-    status[0] = run - valid;
+  // names a real slot and token: blk_bad becomes each chunk's first position
+  // (an exclusive scan over the chunks, 1024 at a time by the whole block).
+  const int valid = base[E - 1] + cnt[E - 1];
+  int run = valid;
+  for (int c0 = 0; c0 < nblk; c0 += 1024) {
+    const int b = c0 + threadIdx.x;
+    const int h = b < nblk ? blk_bad[b] : 0;
+    const int ex = block_exclusive_scan_1024(h, sh);
+    const int tot = sh[1023];   // inclusive total of this group of chunks
+    __syncthreads();            // read before the next group's scan writes sh
+    if (b < nblk) blk_bad[b] = run + ex;
+    run += tot;
   }
+  if (threadIdx.x == 0) status[0] = run - valid;
 }
 
 // Pass 3: stable scatter.  A chunk is walked in rounds of 256 consecutive
