@@ -77,10 +77,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nblk, int E, int b
   const int te = threadIdx.x % E, ts = threadIdx.x / E;
   const bool slice_thread = threadIdx.x < slices * E;
   const int b0 = ts * per, b1 = min(nblk, b0 + per);
-  // The chunk loops load 8 entries before using any, so a thread waits for
-  // one round trip per 8 chunks rather than per chunk (the sums are integer,
+  // The chunk loops load 16 entries before using any, so a thread waits for
+  // one round trip per 16 chunks rather than per chunk (the sums are integer,
   // so the grouping changes nothing).
-  constexpr int U = 8;
+  constexpr int U = 16;
   if (slice_thread) {
     int sum = 0;
     int b = b0;
@@ -430,8 +430,19 @@ __global__ __launch_bounds__(256) void topkw_reduce_kernel(const float* __restri
   if (s >= S) return;
   const int p = inv_pos[s];
   float a = 0.f;
-  if (p >= 0)
-    for (int j = 0; j < nparts; ++j) a += partials[(long)p * nparts + j];
+  if (p >= 0) {
+    // 8 partials loaded before they are added, in the same order
+    const float* row = partials + (long)p * nparts;
+    int j = 0;
+    for (; j + 8 <= nparts; j += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = row[j + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a += v[u];
+    }
+    for (; j < nparts; ++j) a += row[j];
+  }
   dw[s] = a;
 }
 
