@@ -318,7 +318,7 @@ __device__ __forceinline__ void pp_land(int kt, int last, uint16_t* St, int wave
 template <class C, bool A_MN, bool B_MN, bool ZERO, int H, class AS, class BS>
 __device__ __forceinline__ void pp_step(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc, uint16_t* Sp,
                                         uint16_t* Sn, f32x16 (&acc)[C::FM][C::FN], bool hi, int wave, int wm, int wn,
-                                        int lane, int klast) {
+                                        int lane, int klast, bool idle) {
   if (H == 0 && !hi) pp_land<C, ZERO>(kt, last, Sc, wave, lane, klast);
   // The reads below stay below this barrier and the previous sub-step's
   // MFMAs above it (the compiler does not treat s_barrier as a fence).
@@ -329,27 +329,38 @@ __device__ __forceinline__ void pp_step(const AS& as, const BS& bs, int kt, int 
   __builtin_amdgcn_sched_barrier(0);
   if (H == 0) dma_issue<C>(as, bs, min(kt + C::NSTAGE - 1, last), Sp, wave);
   DFrags<C> f0, f1;
-  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 2 * H, f0, wm, wn, lane);
-  dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 2 * H + 1, f1, wm, wn, lane);
+  if (!idle) {
+    dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 2 * H, f0, wm, wn, lane);
+    dma_read<C, A_MN, B_MN>(Sc, Sc + C::A_ELEMS, 2 * H + 1, f1, wm, wn, lane);
+  }
   if (H == C::SUB - 1 && hi) pp_land<C, ZERO>(kt + 1, last, Sn, wave, lane, klast);
   __builtin_amdgcn_sched_barrier(0);   // no MFMA moves above the barrier
   __builtin_amdgcn_s_barrier();   // lower half: B_q; upper half: A_q+1
   __builtin_amdgcn_sched_barrier(0);
-  dma_mma<C>(f0, acc);
-  dma_mma<C>(f1, acc);
+  if (!idle) {
+    dma_mma<C>(f0, acc);
+    dma_mma<C>(f1, acc);
+  }
 }
 
 // Every sub-step of stage kt (buffers Sc, Sp, Sn as in pp_step).
 template <class C, bool A_MN, bool B_MN, bool ZERO, class AS, class BS>
 __device__ __forceinline__ void pp_stage(const AS& as, const BS& bs, int kt, int last, uint16_t* Sc, uint16_t* Sp,
                                          uint16_t* Sn, f32x16 (&acc)[C::FM][C::FN], bool hi, int wave, int wm, int wn,
-                                         int lane, int klast) {
-  pp_step<C, A_MN, B_MN, ZERO, 0>(as, bs, kt, last, Sc, Sp, Sn, acc, hi, wave, wm, wn, lane, klast);
+                                         int lane, int klast, bool idle) {
+  pp_step<C, A_MN, B_MN, ZERO, 0>(as, bs, kt, last, Sc, Sp, Sn, acc, hi, wave, wm, wn, lane, klast, idle);
   if constexpr (C::SUB == 2)
-    pp_step<C, A_MN, B_MN, ZERO, 1>(as, bs, kt, last, Sc, Sp, Sn, acc, hi, wave, wm, wn, lane, klast);
+    pp_step<C, A_MN, B_MN, ZERO, 1>(as, bs, kt, last, Sc, Sp, Sn, acc, hi, wave, wm, wn, lane, klast, idle);
 }
 
 // acc = A . B^T over nk stages of C::BK k; St are the kernel's stage arrays.
+// A wave whose whole block lies past the tile's valid rows or columns
+// (idle, wave-uniform) still issues its share of the loads and passes every
+// barrier but reads no fragments and issues no MFMAs (its accumulators stay
+// zero): on the Zipf batch, whose H = I = 2880 leaves 64 valid columns in
+// the last 256-wide N tile, the token-row kernels ran 1-1.5 % faster.  The
+// weight gradients keep every wave busy (idle there made wgrad_gate_up 3 %
+// slower).
 // Ends with every wave past its last LDS read and the wave's own loads
 // landed.  The last NS - 1 stages still refill stages (with the last stage's
 // data, so that the wait counts stay constant): another wave's refill can
@@ -358,7 +369,7 @@ __device__ __forceinline__ void pp_stage(const AS& as, const BS& bs, int kt, int
 template <class C, bool A_MN, bool B_MN, bool ZERO = false, class AS, class BS>
 __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, uint16_t* const (&St)[5],
                                             f32x16 (&acc)[C::FM][C::FN], int wave, int wm, int wn, int lane,
-                                            int klast = C::BK) {
+                                            int klast, bool idle) {
   static_assert(C::WM == 2, "two row halves of waves");
   constexpr int NS = C::NSTAGE;
 #pragma unroll
@@ -380,13 +391,13 @@ __device__ __forceinline__ void pp_mainloop(const AS& as, const BS& bs, int nk, 
 #pragma unroll
     for (int u = 0; u < NS; ++u)
       pp_stage<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
-                                    wave, wm, wn, lane, klast);
+                                    wave, wm, wn, lane, klast, idle);
   }
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
     if (kt + u < nk)
       pp_stage<C, A_MN, B_MN, ZERO>(as, bs, kt + u, last, St[u], St[(u + NS - 1) % NS], St[(u + 1) % NS], acc, hi,
-                                    wave, wm, wn, lane, klast);
+                                    wave, wm, wn, lane, klast, idle);
   if (!hi) __builtin_amdgcn_s_barrier();   // the upper half's last A barrier
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 }
@@ -570,7 +581,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_kernel(GArgs g) {
       o = (uint32_t)((size_t)g.gu_rs * j * 2);
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, false>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, false>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane, C::BK,
+                                 wm * C::WTM >= rows || j0 + wn * (C::WTN / 2) >= I);
     float* st[4];
     epi_regions<C>(St, st);
     // lane l: activation columns j0 + 2l, 2l + 1, i.e. tile columns c, c + 1
@@ -622,7 +634,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_kernel(GArgs g) {
       o = (uint32_t)((size_t)min(n0 + r, H - 1) * I * 2);
     }, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, false>(as, bs, I / C::BK, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, false>(as, bs, I / C::BK, St, acc, wave, wm, wn, lane, C::BK,
+                                 wm * C::WTM >= rows || n0 + wn * C::WTN >= H);
     float* st[4];
     epi_regions<C>(St, st);
     // Y fp32 [S,H] = routing weight * (a . Wd^T); lane l: columns n0 + 4l .. +3
@@ -770,7 +783,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_down_dgrad_kernel(GArgs g) {
     }, wave, lane);
     bs.init(W, W, I, H, I, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, true>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, true>(as, bs, H / C::BK, St, acc, wave, wm, wn, lane, C::BK,
+                                wm * C::WTM >= rows || n0 + wn * C::WTN >= I);
     float* st[4];
     epi_regions<C>(St, st);
     dma_epi_down_dgrad<C, 2, ACT, LAYOUT>(g, acc, m0, rows, n0, nt, wave, wm, wn, lane, st);
@@ -800,7 +814,8 @@ __global__ __launch_bounds__(C::NT, 1) void dma_gate_up_dgrad_kernel(GArgs g) {
     if (g.gu_sep) bs.init(bg, bu, H, I, H, n0, wave, lane);
     else bs.init(bg, bg, H, I2, H, n0, wave, lane);
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, false, true>(as, bs, I2 / C::BK, St, acc, wave, wm, wn, lane);
+    pp_mainloop<C, false, true>(as, bs, I2 / C::BK, St, acc, wave, wm, wn, lane, C::BK,
+                                wm * C::WTM >= rows || n0 + wn * C::WTN >= H);
     float* st[4];
     epi_regions<C>(St, st);
     // dXp fp32 [S,H]; lane l: columns n0 + 4l .. +3
@@ -865,7 +880,7 @@ __global__ __launch_bounds__(C::NT, 1) void dma_wgrad_kernel(GArgs g) {
     bs.init(Be, Be, N, 0, N, n0, wave, lane, cnt - 1);
     const int nk = (cnt + C::BK - 1) / C::BK;
     f32x16 acc[C::FM][C::FN];
-    pp_mainloop<C, true, true, true>(as, bs, nk, St, acc, wave, wm, wn, lane, cnt - (nk - 1) * C::BK);
+    pp_mainloop<C, true, true, true>(as, bs, nk, St, acc, wave, wm, wn, lane, cnt - (nk - 1) * C::BK, false);
     float* st[4];
     epi_regions<C>(St, st);
     // through LDS, whole row segments (512 bytes bf16, 1 KB fp32), written
