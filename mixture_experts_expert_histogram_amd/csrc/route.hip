@@ -456,6 +456,7 @@ hipError_t launch_topkw_reduce(const float* partials, int nparts, const int32_t*
 
 // ---------------------------------------------------------------------------
 // Gather token rows into expert-sorted order: dst[p] = src[tok_of_pos[p]].
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ src,
                                                           const int32_t* __restrict__ tok, int S, int chunks,
                                                           uint4* __restrict__ dst) {
@@ -463,7 +464,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (long)gridDim.x * blockDim.x) {
     const int p = (int)(idx / chunks);
     const int c = (int)(idx - (long)p * chunks);
-    dst[idx] = src[(long)tok[p] * chunks + c];
+    const uint4 v = src[(long)tok[p] * chunks + c];   // token rows are read K times: the copies stream past L2
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)(dst + idx));
   }
 }
 
